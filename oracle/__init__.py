@@ -1,0 +1,28 @@
+"""Plain float64 CPU oracle for hybrid GQA / sliding-window / DuoAttention
+attention.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the library imports this package; only
+``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may use it. It shares no code with the HIP path.
+
+Every function states the passage of the pages it follows:
+
+* Hugging Face model card "DuoAttention Laguna Adapter" (sections "Summary",
+  "Why It Works", "Changes In This Submission") -- full-context KV heads keep
+  every earlier token; streaming KV heads keep sink tokens plus the most recent
+  tokens (sink 64, recent 256); head routing is per KV head.
+* Blog post on Laguna-M.1-8bit attention, sections on how the sliding window
+  works, its implementation (per-layer ``layer_types`` / ``sliding_window``)
+  and mask generation (``create_causal_mask`` /
+  ``create_sliding_window_causal_mask``) -- a token attends a fixed window of
+  preceding tokens; full layers are causal.
+* SGLang cookbook "Laguna-XS-2.1", section 1 "Model Introduction" -- 48 Q /
+  8 KV heads, window 512.
+
+Readings where the pages are silent are listed in ``oracle.attention``.
+"""
+from .attention import (  # noqa: F401
+    FULL_LAYER, SLIDING_LAYER, bf16_bits_to_f64, kv_head_of, head_is_streaming,
+    visible_positions, attend, prefill_rows, decode_rows,
+)
+from .cache_model import ShadowCache  # noqa: F401
