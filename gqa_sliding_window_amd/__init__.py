@@ -1,0 +1,277 @@
+"""Python binding of the duo_attn C ABI (include/duo_attn.h).
+
+Argument marshalling only: every step of the attention path runs in the HIP
+kernels of libduoattn.so. Torch tensors supply device pointers and the
+current HIP stream. There is no fallback: if the library is missing, every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libduoattn.so")
+
+FULL = 0
+SLIDING = 1
+HEAD_DIM = 128
+
+DUO_OK = 0
+ERRORS = {-1: "DUO_ERR_INVALID_ARG", -2: "DUO_ERR_UNSUPPORTED", -3: "DUO_ERR_CAPACITY",
+          -4: "DUO_ERR_WORKSPACE", -5: "DUO_ERR_HIP"}
+
+
+class DuoError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"{ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("kind", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("sink", ctypes.c_int32), ("recent", ctypes.c_int32),
+                ("full_attention_heads", ctypes.POINTER(ctypes.c_uint8)), ("scale", ctypes.c_float)]
+
+
+class _Cache(ctypes.Structure):
+    _fields_ = [("k_main", ctypes.c_void_p), ("v_main", ctypes.c_void_p),
+                ("main_capacity", ctypes.c_int64),
+                ("k_stream", ctypes.c_void_p), ("v_stream", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH):
+    """Load libduoattn.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with gqa_sliding_window_amd.build.build()")
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    LP, CP = ctypes.POINTER(_Layer), ctypes.POINTER(_Cache)
+    I32P, I64P = ctypes.POINTER(i32), ctypes.POINTER(i64)
+    sigs = {
+        "duo_kv_append": (ctypes.c_int, [LP, CP, i32, P, P, i32, P, i64, P]),
+        "duo_attn_prefill": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, i64, P, P, P]),
+        "duo_attn_decode": (ctypes.c_int, [LP, CP, i32, P, P, i64, P, P, P, sz, P]),
+        "duo_attn_decode_workspace_bytes": (sz, [LP, i32, i64]),
+        "duo_kv_cache_bytes": (ctypes.c_int, [LP, i32, i64, I64P, I64P]),
+        "duo_head_plan": (ctypes.c_int, [LP, I32P, I32P, I32P, I32P]),
+        "duo_prefill_plan": (ctypes.c_int, [LP, i32, i32, i64, I32P, I64P]),
+        "duo_decode_plan": (ctypes.c_int, [LP, i32, i64, I32P, I32P, I64P]),
+        "duo_last_error": (ctypes.c_char_p, []),
+        "duo_attn_version": (ctypes.c_int, []),
+    }
+    for name, (res, args) in sigs.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def _check(rc: int):
+    if rc != DUO_OK:
+        raise DuoError(rc, load().duo_last_error().decode())
+
+
+@dataclass
+class Layer:
+    """One attention layer (see duo_layer in include/duo_attn.h)."""
+    num_q_heads: int = 48
+    num_kv_heads: int = 8
+    kind: int = FULL
+    window: int = 0
+    sink: int = 64
+    recent: int = 256
+    full_attention_heads: Optional[Sequence[int]] = None
+    scale: float = 0.0
+    head_dim: int = HEAD_DIM
+
+    def _c(self):
+        mask = None
+        if self.full_attention_heads is not None:
+            arr = (ctypes.c_uint8 * len(self.full_attention_heads))(*[int(x) for x in self.full_attention_heads])
+            mask = ctypes.cast(arr, ctypes.POINTER(ctypes.c_uint8))
+            self._keep = arr  # keep alive for the call
+        return _Layer(self.num_q_heads, self.num_kv_heads, self.head_dim, self.kind, self.window,
+                      self.sink, self.recent, mask, float(self.scale))
+
+    @property
+    def n_main(self) -> int:
+        if self.full_attention_heads is None:
+            return self.num_kv_heads
+        return sum(1 for x in self.full_attention_heads if int(x) != 0)
+
+    @property
+    def n_stream(self) -> int:
+        return self.num_kv_heads - self.n_main
+
+    @property
+    def main_ring(self) -> bool:
+        return self.kind == SLIDING and self.window > 0
+
+
+def _ptr(t) -> int:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+class KVCache:
+    """A layer's static KV cache in device memory (torch tensors, bf16)."""
+
+    def __init__(self, layer: Layer, batch: int, capacity: int, device="cuda", zero=True):
+        import torch
+        self.layer = layer
+        self.batch = batch
+        self.capacity = layer.window if layer.main_ring else capacity
+        alloc = torch.zeros if zero else torch.empty
+        nm, ns = layer.n_main, layer.n_stream
+        sr = layer.sink + layer.recent
+        self.k_main = alloc((batch, nm, self.capacity, HEAD_DIM), dtype=torch.bfloat16, device=device) if nm else None
+        self.v_main = alloc((batch, nm, self.capacity, HEAD_DIM), dtype=torch.bfloat16, device=device) if nm else None
+        self.k_stream = alloc((batch, ns, sr, HEAD_DIM), dtype=torch.bfloat16, device=device) if ns else None
+        self.v_stream = alloc((batch, ns, sr, HEAD_DIM), dtype=torch.bfloat16, device=device) if ns else None
+
+    def _c(self, batch_offset: int = 0):
+        def off(t):
+            if t is None:
+                return None
+            return t[batch_offset].data_ptr() if batch_offset else t.data_ptr()
+        return _Cache(off(self.k_main), off(self.v_main), self.capacity,
+                      off(self.k_stream), off(self.v_stream))
+
+
+def kv_append(layer: Layer, cache: KVCache, k_new, v_new, start_pos, max_end_pos: int,
+              batch: Optional[int] = None, batch_offset: int = 0, stream=None):
+    """duo_kv_append: k_new/v_new [B, T, Hkv, 128] bf16, start_pos int32 [B] (device)."""
+    lib = load()
+    B = k_new.shape[0] if batch is None else batch
+    T = k_new.shape[1]
+    cl, cc = layer._c(), cache._c(batch_offset)
+    _check(lib.duo_kv_append(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(k_new), _ptr(v_new), T,
+                             _ptr(start_pos), int(max_end_pos), _stream(stream)))
+
+
+def attn_prefill(layer: Layer, q, k, v, out, start_pos: int = 0, past: Optional[KVCache] = None,
+                 lse=None, stream=None):
+    """duo_attn_prefill: q [B, T, Hq, 128], k/v [B, T, Hkv, 128], out like q."""
+    lib = load()
+    B, T = q.shape[0], q.shape[1]
+    cl = layer._c()
+    cc = past._c() if past is not None else None
+    _check(lib.duo_attn_prefill(ctypes.byref(cl), ctypes.byref(cc) if cc is not None else None, B,
+                                _ptr(q), _ptr(k), _ptr(v), T, int(start_pos), _ptr(out), _ptr(lse),
+                                _stream(stream)))
+
+
+def decode_workspace_bytes(layer: Layer, batch: int, max_seq_len: int) -> int:
+    cl = layer._c()
+    return int(load().duo_attn_decode_workspace_bytes(ctypes.byref(cl), batch, int(max_seq_len)))
+
+
+def attn_decode(layer: Layer, cache: KVCache, q, seq_lens, max_seq_len: int, out, workspace,
+                lse=None, stream=None):
+    """duo_attn_decode: q [B, Hq, 128], seq_lens int32 [B] (device), out like q."""
+    lib = load()
+    B = q.shape[0]
+    cl, cc = layer._c(), cache._c()
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.duo_attn_decode(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(q), _ptr(seq_lens),
+                               int(max_seq_len), _ptr(out), _ptr(lse), _ptr(workspace), nbytes,
+                               _stream(stream)))
+
+
+def head_plan(layer: Layer):
+    lib = load()
+    n = layer.num_kv_heads
+    cls, rank = (ctypes.c_int32 * n)(), (ctypes.c_int32 * n)()
+    nm, ns = ctypes.c_int32(), ctypes.c_int32()
+    cl = layer._c()
+    _check(lib.duo_head_plan(ctypes.byref(cl), cls, rank, ctypes.byref(nm), ctypes.byref(ns)))
+    return list(cls), list(rank), nm.value, ns.value
+
+
+def prefill_plan(layer: Layer, batch: int, num_tokens: int, start_pos: int = 0):
+    """Per workgroup (batch, q_head, q_tile, key_tiles); padding rows are -1."""
+    import numpy as np
+    lib = load()
+    cl = layer._c()
+    n = ctypes.c_int64()
+    _check(lib.duo_prefill_plan(ctypes.byref(cl), batch, num_tokens, start_pos, None, ctypes.byref(n)))
+    items = np.zeros((n.value, 4), dtype=np.int32)
+    _check(lib.duo_prefill_plan(ctypes.byref(cl), batch, num_tokens, start_pos,
+                                items.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(n)))
+    return items
+
+
+def decode_plan(layer: Layer, batch: int, max_seq_len: int):
+    """(split_keys, items[n, 4] = (batch, kv_head, split, class))."""
+    import numpy as np
+    lib = load()
+    cl = layer._c()
+    n, sk = ctypes.c_int64(), ctypes.c_int32()
+    _check(lib.duo_decode_plan(ctypes.byref(cl), batch, max_seq_len, ctypes.byref(sk), None, ctypes.byref(n)))
+    items = np.zeros((n.value, 4), dtype=np.int32)
+    _check(lib.duo_decode_plan(ctypes.byref(cl), batch, max_seq_len, ctypes.byref(sk),
+                               items.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(n)))
+    return sk.value, items
+
+
+def kv_cache_bytes(layer: Layer, batch: int, capacity: int):
+    lib = load()
+    cl = layer._c()
+    a, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(lib.duo_kv_cache_bytes(ctypes.byref(cl), batch, capacity, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def prefill_flops(layer: Layer, batch: int, num_tokens: int, start_pos: int = 0) -> int:
+    """Algorithmic FLOP: 4 * D per (query row, visible key) pair, over all
+    batch x Hq rows (masked pairs are not counted)."""
+    g = layer.num_q_heads // layer.num_kv_heads
+    total = 0
+    for kvh in range(layer.num_kv_heads):
+        streaming = layer.full_attention_heads is not None and int(layer.full_attention_heads[kvh]) == 0
+        total += g * visible_pairs(layer, streaming, start_pos, num_tokens)
+    return 4 * HEAD_DIM * batch * total
+
+
+def visible_pairs(layer: Layer, streaming: bool, start_pos: int, num_tokens: int) -> int:
+    """Sum over query positions i in [start_pos, start_pos+T) of |Vis(i)|
+    (closed forms: min(i+1, W), min(i+1, S+R) or i+1)."""
+    def s_min(cap):  # sum_{i=a}^{b} min(i+1, cap)
+        a, b = start_pos, start_pos + num_tokens - 1
+        tot = 0
+        lo_lin = a
+        hi_lin = min(b, cap - 1)
+        if hi_lin >= lo_lin:
+            tot += (lo_lin + 1 + hi_lin + 1) * (hi_lin - lo_lin + 1) // 2
+        flat_lo = max(a, cap)
+        if b >= flat_lo:
+            tot += cap * (b - flat_lo + 1)
+        return tot
+    if streaming:
+        return s_min(layer.sink + layer.recent)
+    if layer.main_ring:
+        return s_min(layer.window)
+    a, b = start_pos, start_pos + num_tokens - 1
+    return (a + 1 + b + 1) * (b - a + 1) // 2

@@ -1,0 +1,409 @@
+// Host side of the duo_attn C ABI: argument validation (synchronous, no side
+// effects on error), the head-class and work plans, and kernel launches on the
+// caller's stream. See include/duo_attn.h for the contract of every entry.
+#include "duo_attn.h"
+#include "duo_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+using namespace duo;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return DUO_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int64_t kMaxPos = 0x7FFFFFFF;   // positions are int32 on the device side
+constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // workgroups per launch
+
+struct Layer {
+  int hq, hkv, group, kind, window, sink, recent;
+  float scale;
+  bool main_ring;     // main cache is a ring of `window` slots
+  int main_window;    // causal band of main-class heads (0 = none)
+  HeadPlan plan;
+};
+
+// Validate a layer description and build its head-class plan (model card
+// "DuoAttention Laguna Adapter", "Summary": full-context vs. streaming KV
+// heads, one decision per KV head).
+int check_layer(const duo_layer* L, Layer* out) {
+  if (L == nullptr) return fail(DUO_ERR_INVALID_ARG, "layer is NULL");
+  if (L->head_dim != kD) return fail(DUO_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", L->head_dim);
+  if (L->num_q_heads <= 0 || L->num_kv_heads <= 0)
+    return fail(DUO_ERR_INVALID_ARG, "head counts must be positive (q %d, kv %d)", L->num_q_heads, L->num_kv_heads);
+  if (L->num_q_heads % L->num_kv_heads != 0)
+    return fail(DUO_ERR_INVALID_ARG, "num_q_heads %d is not a multiple of num_kv_heads %d", L->num_q_heads, L->num_kv_heads);
+  if (L->num_kv_heads > kMaxKv) return fail(DUO_ERR_UNSUPPORTED, "num_kv_heads %d > %d", L->num_kv_heads, kMaxKv);
+  const int group = L->num_q_heads / L->num_kv_heads;
+  if (group > DUO_MAX_GROUP) return fail(DUO_ERR_UNSUPPORTED, "group size %d > %d", group, DUO_MAX_GROUP);
+  if (L->kind != DUO_LAYER_FULL && L->kind != DUO_LAYER_SLIDING)
+    return fail(DUO_ERR_INVALID_ARG, "unknown layer kind %d", L->kind);
+  if (L->sink < 0 || L->recent < 0) return fail(DUO_ERR_INVALID_ARG, "sink %d / recent %d must be >= 0", L->sink, L->recent);
+  if (!(L->scale >= 0.f) || std::isinf(L->scale)) return fail(DUO_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  Layer r{};
+  r.hq = L->num_q_heads;
+  r.hkv = L->num_kv_heads;
+  r.group = group;
+  r.kind = L->kind;
+  r.window = L->window;
+  r.sink = L->sink;
+  r.recent = L->recent;
+  r.scale = L->scale > 0.f ? L->scale : 1.f / std::sqrt((float)kD);
+  r.main_ring = (L->kind == DUO_LAYER_SLIDING && L->window > 0);
+  r.main_window = r.main_ring ? L->window : 0;
+  std::memset(&r.plan, -1, sizeof(r.plan));
+  r.plan.n_main = r.plan.n_stream = 0;
+  r.plan.stream_mask = 0;
+  for (int h = 0; h < r.hkv; ++h) {
+    const bool streaming = L->full_attention_heads != nullptr && L->full_attention_heads[h] == 0;
+    if (streaming) {
+      r.plan.stream_mask |= 1u << h;
+      r.plan.stream_heads[r.plan.n_stream++] = (int8_t)h;
+    } else {
+      r.plan.main_heads[r.plan.n_main++] = (int8_t)h;
+    }
+  }
+  if (r.plan.n_stream > 0 && r.recent < 1)
+    return fail(DUO_ERR_INVALID_ARG, "streaming heads need recent >= 1 (the current token is always kept)");
+  if (r.plan.n_stream > 0 && (int64_t)r.sink + r.recent > kMaxPos)
+    return fail(DUO_ERR_INVALID_ARG, "sink + recent too large");
+  *out = r;
+  return DUO_OK;
+}
+
+int check_cache(const Layer& L, const duo_kv_cache* c, bool need_main, bool need_stream) {
+  if (c == nullptr) return fail(DUO_ERR_INVALID_ARG, "cache is NULL");
+  if (need_main && L.plan.n_main > 0) {
+    if (c->k_main == nullptr || c->v_main == nullptr) return fail(DUO_ERR_INVALID_ARG, "main cache pointers are NULL");
+    if (!aligned16(c->k_main) || !aligned16(c->v_main)) return fail(DUO_ERR_INVALID_ARG, "main cache pointers must be 16-byte aligned");
+    if (c->main_capacity <= 0) return fail(DUO_ERR_INVALID_ARG, "main_capacity must be > 0");
+    if (L.main_ring && c->main_capacity != L.window)
+      return fail(DUO_ERR_INVALID_ARG, "sliding-layer ring must have main_capacity == window (%lld vs %d)",
+                  (long long)c->main_capacity, L.window);
+  }
+  if (need_stream && L.plan.n_stream > 0) {
+    if (c->k_stream == nullptr || c->v_stream == nullptr) return fail(DUO_ERR_INVALID_ARG, "stream cache pointers are NULL");
+    if (!aligned16(c->k_stream) || !aligned16(c->v_stream)) return fail(DUO_ERR_INVALID_ARG, "stream cache pointers must be 16-byte aligned");
+  }
+  return DUO_OK;
+}
+
+void fill_heads(const Layer& L, int8_t* main_heads, int8_t* stream_heads) {
+  std::memcpy(main_heads, L.plan.main_heads, kMaxKv);
+  std::memcpy(stream_heads, L.plan.stream_heads, kMaxKv);
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(DUO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// ---- prefill plan
+int build_prefill(const Layer& L, int32_t batch, int32_t T, int64_t start_pos, PrefillParams* p,
+                  int64_t* n_blocks) {
+  std::memset(p, 0, sizeof(*p));
+  p->start_pos = start_pos;
+  p->batch = batch;
+  p->T = T;
+  p->hq = L.hq;
+  p->hkv = L.hkv;
+  p->group = L.group;
+  p->main_window = L.main_window;
+  p->main_ring = L.main_ring ? 1 : 0;
+  p->sink = L.sink;
+  p->recent = L.recent;
+  p->n_main = L.plan.n_main;
+  p->n_stream = L.plan.n_stream;
+  p->stream_mask = L.plan.stream_mask;
+  p->n_qtiles = (T + kPrefillRows - 1) / kPrefillRows;
+  const int64_t um = (int64_t)p->n_qtiles * batch * L.plan.n_main;
+  const int64_t us = (int64_t)p->n_qtiles * batch * L.plan.n_stream;
+  if (um + us > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "prefill work too large for one launch");
+  p->n_units_main = (int32_t)um;
+  p->n_units = (int32_t)(um + us);
+  p->scale_log2 = L.scale * 1.4426950408889634f;
+  fill_heads(L, p->main_heads, p->stream_heads);
+  const int64_t units8 = (p->n_units + kXcds - 1) / kXcds * kXcds;
+  *n_blocks = units8 * L.group;
+  if (*n_blocks > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "prefill grid too large");
+  return DUO_OK;
+}
+
+// ---- decode plan: keys per split chosen so the launch has about
+// kDecodeTargetItems work items (8192 waves would be 32 per CU), never
+// fewer than kDecodeMinSplit keys per split.
+int build_decode(const Layer& L, int32_t batch, int64_t max_seq_len, int64_t main_cap, DecodeParams* p) {
+  std::memset(p, 0, sizeof(*p));
+  p->batch = batch;
+  p->hq = L.hq;
+  p->hkv = L.hkv;
+  p->group = L.group;
+  p->main_ring = L.main_ring ? 1 : 0;
+  p->main_cap = main_cap;
+  p->sink = L.sink;
+  p->recent = L.recent;
+  p->n_main = L.plan.n_main;
+  p->n_stream = L.plan.n_stream;
+  p->stream_mask = L.plan.stream_mask;
+  p->scale_log2 = L.scale * 1.4426950408889634f;
+  fill_heads(L, p->main_heads, p->stream_heads);
+  const int64_t keys_main = L.main_ring ? (max_seq_len < L.window ? max_seq_len : L.window) : max_seq_len;
+  const int64_t sr = (int64_t)L.sink + L.recent;
+  const int64_t keys_stream = max_seq_len < sr ? max_seq_len : sr;
+  const int64_t total = (int64_t)batch * (L.plan.n_main * keys_main + L.plan.n_stream * keys_stream);
+  int64_t split = (total + kDecodeTargetItems - 1) / kDecodeTargetItems;
+  split = (split + kDecodeKeys - 1) / kDecodeKeys * kDecodeKeys;
+  if (split < kDecodeMinSplit) split = kDecodeMinSplit;
+  if (split > kMaxPos) split = kMaxPos / kDecodeKeys * kDecodeKeys;
+  p->split_keys = (int32_t)split;
+  p->n_split_main = L.plan.n_main > 0 ? (int32_t)((keys_main + split - 1) / split) : 0;
+  p->n_split_stream = L.plan.n_stream > 0 ? (int32_t)((keys_stream + split - 1) / split) : 0;
+  if (p->n_split_main < 1 && L.plan.n_main > 0) p->n_split_main = 1;
+  if (p->n_split_stream < 1 && L.plan.n_stream > 0) p->n_split_stream = 1;
+  p->n_split_max = p->n_split_main > p->n_split_stream ? p->n_split_main : p->n_split_stream;
+  const int64_t im = (int64_t)batch * L.plan.n_main * p->n_split_main;
+  const int64_t is = (int64_t)batch * L.plan.n_stream * p->n_split_stream;
+  if (im + is > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "decode work too large for one launch");
+  p->n_items_main = (int32_t)im;
+  p->n_items = (int32_t)(im + is);
+  return DUO_OK;
+}
+
+size_t decode_ws_bytes(const DecodeParams& p) {
+  const size_t n = (size_t)p.batch * p.hq * (size_t)p.n_split_max;
+  const size_t acc = n * kD * sizeof(float);
+  const size_t acc_padded = (acc + 255) / 256 * 256;
+  return acc_padded + n * 2 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int duo_attn_version(void) { return DUO_ATTN_VERSION; }
+
+const char* duo_last_error(void) { return g_err; }
+
+int duo_head_plan(const duo_layer* layer, int32_t* head_class, int32_t* head_rank_out, int32_t* n_main,
+                  int32_t* n_stream) {
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  for (int h = 0; h < L.hkv; ++h) {
+    const bool s = (L.plan.stream_mask >> h) & 1u;
+    if (head_class) head_class[h] = s ? 1 : 0;
+    if (head_rank_out) head_rank_out[h] = head_rank(L.plan.stream_mask, h);
+  }
+  if (n_main) *n_main = L.plan.n_main;
+  if (n_stream) *n_stream = L.plan.n_stream;
+  return ok();
+}
+
+int duo_kv_cache_bytes(const duo_layer* layer, int32_t batch, int64_t capacity, int64_t* main_bytes,
+                       int64_t* stream_bytes) {
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  if (batch < 0 || capacity < 0) return fail(DUO_ERR_INVALID_ARG, "batch and capacity must be >= 0");
+  const int64_t main_slots = L.main_ring ? L.window : capacity;
+  const int64_t row = kD * 2;
+  if (main_bytes) *main_bytes = (int64_t)batch * L.plan.n_main * main_slots * row;
+  if (stream_bytes) *stream_bytes = (int64_t)batch * L.plan.n_stream * ((int64_t)L.sink + L.recent) * row;
+  return ok();
+}
+
+int duo_kv_append(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch, const void* k_new,
+                  const void* v_new, int32_t num_tokens, const int32_t* start_pos, int64_t max_end_pos,
+                  void* stream) {
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  if (batch < 0 || num_tokens < 0) return fail(DUO_ERR_INVALID_ARG, "batch and num_tokens must be >= 0");
+  if (batch == 0 || num_tokens == 0) return ok();
+  if ((rc = check_cache(L, cache, true, true))) return rc;
+  if (k_new == nullptr || v_new == nullptr || start_pos == nullptr)
+    return fail(DUO_ERR_INVALID_ARG, "k_new, v_new and start_pos must not be NULL");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(DUO_ERR_INVALID_ARG, "k_new/v_new must be 16-byte aligned");
+  if (max_end_pos < num_tokens || max_end_pos > kMaxPos)
+    return fail(DUO_ERR_INVALID_ARG, "max_end_pos %lld out of range", (long long)max_end_pos);
+  if (L.plan.n_main > 0 && !L.main_ring && max_end_pos > cache->main_capacity)
+    return fail(DUO_ERR_CAPACITY, "positions up to %lld exceed main_capacity %lld", (long long)max_end_pos,
+                (long long)cache->main_capacity);
+  if ((int64_t)batch * num_tokens * L.hkv / 16 + 1 > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "append too large");
+  AppendParams p{};
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.start_pos = start_pos;
+  p.k_main = static_cast<uint16_t*>(cache->k_main);
+  p.v_main = static_cast<uint16_t*>(cache->v_main);
+  p.k_stream = static_cast<uint16_t*>(cache->k_stream);
+  p.v_stream = static_cast<uint16_t*>(cache->v_stream);
+  p.main_cap = cache->main_capacity;
+  p.batch = batch;
+  p.T = num_tokens;
+  p.hkv = L.hkv;
+  p.main_ring = L.main_ring ? 1 : 0;
+  p.sink = L.sink;
+  p.recent = L.recent;
+  p.n_main = L.plan.n_main;
+  p.n_stream = L.plan.n_stream;
+  p.stream_mask = L.plan.stream_mask;
+  return hip_status(launch_kv_append(p, static_cast<hipStream_t>(stream)), "kv_append launch");
+}
+
+int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens, int64_t start_pos,
+                     int32_t* items, int64_t* n_items) {
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  if (batch < 0 || num_tokens < 0 || start_pos < 0) return fail(DUO_ERR_INVALID_ARG, "negative size");
+  if (start_pos + num_tokens > kMaxPos) return fail(DUO_ERR_INVALID_ARG, "positions exceed int32");
+  PrefillParams p;
+  int64_t nb = 0;
+  if (batch > 0 && num_tokens > 0 && (rc = build_prefill(L, batch, num_tokens, start_pos, &p, &nb))) return rc;
+  if (n_items) *n_items = nb;
+  if (items) {
+    for (int64_t i = 0; i < nb; ++i) {
+      const PrefillItem it = prefill_item(p, i);
+      int32_t* o = items + 4 * i;
+      if (!it.valid) { o[0] = o[1] = o[2] = -1; o[3] = 0; continue; }
+      const int64_t qa = start_pos + (int64_t)it.qtile * kPrefillRows;
+      const int64_t last = start_pos + num_tokens - 1;
+      const int64_t qb = qa + kPrefillRows - 1 < last ? qa + kPrefillRows - 1 : last;
+      KeyRange r[2];
+      const int nr = prefill_key_ranges(p, it.cls, qa, qb, r);
+      int64_t tiles = 0;
+      for (int k = 0; k < nr; ++k) tiles += tiles_of(r[k]);
+      o[0] = it.b; o[1] = it.qhead; o[2] = it.qtile; o[3] = (int32_t)tiles;
+    }
+  }
+  return ok();
+}
+
+int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t batch, const void* q,
+                     const void* k, const void* v, int32_t num_tokens, int64_t start_pos, void* out,
+                     float* lse, void* stream) {
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  if (batch < 0 || num_tokens < 0 || start_pos < 0) return fail(DUO_ERR_INVALID_ARG, "negative size or start_pos");
+  if (start_pos + num_tokens > kMaxPos) return fail(DUO_ERR_INVALID_ARG, "positions exceed int32");
+  if (batch == 0 || num_tokens == 0) return ok();
+  if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
+    return fail(DUO_ERR_INVALID_ARG, "q, k, v and out must not be NULL");
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(DUO_ERR_INVALID_ARG, "q, k, v and out must be 16-byte aligned");
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(DUO_ERR_INVALID_ARG, "lse misaligned");
+  duo_kv_cache none{};
+  if (start_pos > 0) {
+    if (past == nullptr) return fail(DUO_ERR_INVALID_ARG, "start_pos > 0 needs the past cache");
+    if ((rc = check_cache(L, past, true, true))) return rc;
+    if (L.plan.n_main > 0 && !L.main_ring && start_pos > past->main_capacity)
+      return fail(DUO_ERR_CAPACITY, "start_pos %lld exceeds main_capacity %lld", (long long)start_pos,
+                  (long long)past->main_capacity);
+  } else {
+    past = past ? past : &none;
+  }
+  PrefillParams p;
+  int64_t nb = 0;
+  if ((rc = build_prefill(L, batch, num_tokens, start_pos, &p, &nb))) return rc;
+  p.q = static_cast<const uint16_t*>(q);
+  p.k = static_cast<const uint16_t*>(k);
+  p.v = static_cast<const uint16_t*>(v);
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.k_main = static_cast<const uint16_t*>(past->k_main);
+  p.v_main = static_cast<const uint16_t*>(past->v_main);
+  p.k_stream = static_cast<const uint16_t*>(past->k_stream);
+  p.v_stream = static_cast<const uint16_t*>(past->v_stream);
+  p.main_cap = L.main_ring ? L.window : (past->main_capacity > 0 ? past->main_capacity : 1);
+  return hip_status(launch_prefill(p, nb, static_cast<hipStream_t>(stream)), "prefill launch");
+}
+
+size_t duo_attn_decode_workspace_bytes(const duo_layer* layer, int32_t batch, int64_t max_seq_len) {
+  Layer L;
+  if (check_layer(layer, &L)) return 0;
+  if (batch <= 0 || max_seq_len <= 0 || max_seq_len > kMaxPos) return 0;
+  DecodeParams p;
+  if (build_decode(L, batch, max_seq_len, L.main_ring ? L.window : max_seq_len, &p)) return 0;
+  ok();
+  return decode_ws_bytes(p);
+}
+
+int duo_decode_plan(const duo_layer* layer, int32_t batch, int64_t max_seq_len, int32_t* split_keys,
+                    int32_t* items, int64_t* n_items) {
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  if (batch <= 0 || max_seq_len <= 0 || max_seq_len > kMaxPos) return fail(DUO_ERR_INVALID_ARG, "bad batch or max_seq_len");
+  DecodeParams p;
+  if ((rc = build_decode(L, batch, max_seq_len, L.main_ring ? L.window : max_seq_len, &p))) return rc;
+  if (split_keys) *split_keys = p.split_keys;
+  if (n_items) *n_items = p.n_items;
+  if (items) {
+    for (int64_t i = 0; i < p.n_items; ++i) {
+      const DecodeItem it = decode_item(p, i);
+      int32_t* o = items + 4 * i;
+      o[0] = it.b; o[1] = it.kvh; o[2] = it.split; o[3] = it.cls;
+    }
+  }
+  return ok();
+}
+
+int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch, const void* q,
+                    const int32_t* seq_lens, int64_t max_seq_len, void* out, float* lse, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  if (batch < 0) return fail(DUO_ERR_INVALID_ARG, "batch must be >= 0");
+  if (batch == 0) return ok();
+  if (max_seq_len <= 0 || max_seq_len > kMaxPos) return fail(DUO_ERR_INVALID_ARG, "max_seq_len out of range");
+  if (q == nullptr || seq_lens == nullptr || out == nullptr) return fail(DUO_ERR_INVALID_ARG, "q, seq_lens and out must not be NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(DUO_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(DUO_ERR_INVALID_ARG, "lse misaligned");
+  if ((rc = check_cache(L, cache, true, true))) return rc;
+  if (L.plan.n_main > 0 && !L.main_ring && max_seq_len > cache->main_capacity)
+    return fail(DUO_ERR_CAPACITY, "max_seq_len %lld exceeds main_capacity %lld", (long long)max_seq_len,
+                (long long)cache->main_capacity);
+  DecodeParams p;
+  const int64_t main_cap = L.main_ring ? L.window : (L.plan.n_main > 0 ? cache->main_capacity : 1);
+  if ((rc = build_decode(L, batch, max_seq_len, main_cap, &p))) return rc;
+  const size_t need = decode_ws_bytes(p);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DUO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DUO_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  p.q = static_cast<const uint16_t*>(q);
+  p.seq_lens = seq_lens;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.k_main = static_cast<const uint16_t*>(cache->k_main);
+  p.v_main = static_cast<const uint16_t*>(cache->v_main);
+  p.k_stream = static_cast<const uint16_t*>(cache->k_stream);
+  p.v_stream = static_cast<const uint16_t*>(cache->v_stream);
+  const size_t n = (size_t)p.batch * p.hq * (size_t)p.n_split_max;
+  const size_t acc = (n * kD * sizeof(float) + 255) / 256 * 256;
+  p.ws_acc = static_cast<float*>(workspace);
+  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc);
+  return hip_status(launch_decode(p, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,209 @@
+// Internal definitions shared by the host planner and the gfx950 kernels of
+// the duo_attn library: kernel parameter blocks, the head-class plan and the
+// work-item decoders (host and device use the same functions, so the plan the
+// host reports is the plan the kernels execute).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace duo {
+
+constexpr int kD = 128;           // head_dim
+constexpr int kMaxKv = 32;        // KV heads per layer
+constexpr int kPrefillRows = 128; // query rows per prefill workgroup (4 waves x 32)
+constexpr int kPrefillKeys = 64;  // keys per prefill K/V tile
+constexpr int kDecodeKeys = 32;   // keys per decode tile (one wave)
+constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
+constexpr int kDecodeTargetItems = 4096;
+constexpr int kDecodeMinSplit = 128;
+
+enum HeadClass : int { kMain = 0, kStream = 1 };
+
+// Head-class plan of one layer (model card "DuoAttention Laguna Adapter",
+// "Summary": KV heads are full-context or streaming; "Changes In This
+// Submission": heads reordered so the two classes separate). Within a class,
+// heads are ranked by ascending KV-head index.
+struct HeadPlan {
+  int32_t n_main;
+  int32_t n_stream;
+  uint32_t stream_mask;          // bit kvh set = streaming head
+  int8_t main_heads[kMaxKv];     // rank -> kvh
+  int8_t stream_heads[kMaxKv];
+};
+
+__host__ __device__ inline int head_rank(uint32_t stream_mask, int kvh) {
+  const uint32_t below = (kvh == 0) ? 0u : (0xFFFFFFFFu >> (32 - kvh));
+  const bool s = (stream_mask >> kvh) & 1u;
+  return __builtin_popcount((s ? stream_mask : ~stream_mask) & below);
+}
+
+// ---------------------------------------------------------------- kv append
+struct AppendParams {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* start_pos;
+  uint16_t* k_main;
+  uint16_t* v_main;
+  uint16_t* k_stream;
+  uint16_t* v_stream;
+  int64_t main_cap;     // slots per (b, head) in the main cache
+  int32_t batch, T, hkv;
+  int32_t main_ring;    // 1: main cache is a ring of main_cap slots
+  int32_t sink, recent;
+  int32_t n_main, n_stream;
+  uint32_t stream_mask;
+};
+
+// ---------------------------------------------------------------- prefill
+struct PrefillParams {
+  const uint16_t* q;     // [B, T, Hq, D]
+  const uint16_t* k;     // [B, T, Hkv, D]
+  const uint16_t* v;
+  uint16_t* out;         // [B, T, Hq, D]
+  float* lse;            // [B, Hq, T] or null
+  const uint16_t* k_main;
+  const uint16_t* v_main;
+  const uint16_t* k_stream;
+  const uint16_t* v_stream;
+  int64_t main_cap;
+  int64_t start_pos;
+  int32_t batch, T, hq, hkv, group;
+  int32_t main_window;   // > 0: main-class heads see a causal window of this width
+  int32_t main_ring;     // 1: cached main positions live in a ring of main_cap slots
+  int32_t sink, recent;
+  int32_t n_main, n_stream;
+  uint32_t stream_mask;
+  int32_t n_qtiles;
+  int32_t n_units_main;  // (q tile, batch, main head) units
+  int32_t n_units;       // all units
+  float scale_log2;      // scale * log2(e)
+  int8_t main_heads[kMaxKv];
+  int8_t stream_heads[kMaxKv];
+};
+
+struct PrefillItem {
+  int32_t valid;
+  int32_t cls;
+  int32_t b, kvh, rank, qhead, qtile;
+};
+
+// Workgroup -> work item. Units (one 128-row query tile of one KV-head group)
+// are ordered heaviest first: main-class units before streaming units, later
+// query tiles before earlier ones. Unit u runs on XCD u % 8 (workgroups are
+// dispatched to XCDs round-robin), so every XCD gets an equal share of each
+// cost level; the `group` query heads of one unit are consecutive on that XCD
+// and share the unit's K/V tiles through its L2.
+__host__ __device__ inline PrefillItem prefill_item(const PrefillParams& p, int64_t block) {
+  PrefillItem it{};
+  const int64_t x = block % kXcds;
+  const int64_t s = block / kXcds;
+  const int64_t unit = (s / p.group) * kXcds + x;
+  const int g = (int)(s % p.group);
+  if (unit >= p.n_units) { it.valid = 0; return it; }
+  it.valid = 1;
+  int64_t u = unit;
+  int n_class = p.n_main;
+  it.cls = kMain;
+  if (u >= p.n_units_main) { u -= p.n_units_main; it.cls = kStream; n_class = p.n_stream; }
+  const int64_t groups = (int64_t)p.batch * n_class;
+  it.qtile = p.n_qtiles - 1 - (int)(u / groups);
+  const int64_t grp = u % groups;
+  it.b = (int)(grp / n_class);
+  it.rank = (int)(grp % n_class);
+  it.kvh = (it.cls == kMain) ? p.main_heads[it.rank] : p.stream_heads[it.rank];
+  it.qhead = it.kvh * p.group + g;
+  return it;
+}
+
+// Key ranges (absolute positions, inclusive) a work item must visit for its
+// query rows [qa, qb]; span > 0 is the width of a causal band ending at the
+// query (window or recent), 0 = no band. Returns the number of ranges (<= 2).
+struct KeyRange { int64_t lo, hi; int64_t span; };
+
+__host__ __device__ inline int prefill_key_ranges(const PrefillParams& p, int cls, int64_t qa,
+                                                  int64_t qb, KeyRange* r) {
+  int n = 0;
+  if (cls == kMain) {
+    const int64_t w = p.main_window;
+    r[0].lo = (w > 0) ? ((qa - w + 1) > 0 ? (qa - w + 1) : 0) : 0;
+    r[0].hi = qb;
+    r[0].span = (w > 0) ? w : 0;
+    return 1;
+  }
+  // streaming head: sink positions [0, sink) that are <= the query, and the
+  // `recent` positions ending at the query (model card, "Why It Works").
+  if (p.sink > 0) {
+    const int64_t hi = (qb < p.sink - 1) ? qb : (int64_t)p.sink - 1;
+    r[n].lo = 0; r[n].hi = hi; r[n].span = 0; n++;
+  }
+  int64_t lo = qa - p.recent + 1;
+  if (lo < p.sink) lo = p.sink;
+  if (lo <= qb) { r[n].lo = lo; r[n].hi = qb; r[n].span = p.recent; n++; }
+  return n;
+}
+
+__host__ __device__ inline int64_t tiles_of(const KeyRange& r) {
+  return r.hi / kPrefillKeys - r.lo / kPrefillKeys + 1;
+}
+
+// ---------------------------------------------------------------- decode
+struct DecodeParams {
+  const uint16_t* q;     // [B, Hq, D]
+  const int32_t* seq_lens;
+  uint16_t* out;         // [B, Hq, D]
+  float* lse;            // [B, Hq] or null
+  const uint16_t* k_main;
+  const uint16_t* v_main;
+  const uint16_t* k_stream;
+  const uint16_t* v_stream;
+  float* ws_acc;         // [B, Hq, n_split_max, D]
+  float* ws_ml;          // [B, Hq, n_split_max, 2]
+  int64_t main_cap;      // slots per (b, main head)
+  int32_t main_ring;     // main cache is a ring (sliding layer)
+  int32_t batch, hq, hkv, group;
+  int32_t sink, recent;
+  int32_t n_main, n_stream;
+  uint32_t stream_mask;
+  int32_t split_keys;
+  int32_t n_split_main, n_split_stream, n_split_max;
+  int32_t n_items_main, n_items;
+  float scale_log2;
+  int8_t main_heads[kMaxKv];
+  int8_t stream_heads[kMaxKv];
+};
+
+struct DecodeItem { int32_t cls, b, rank, kvh, split; };
+
+// Work item i: main-class items (batch, head rank, split) first, then
+// streaming items.
+__host__ __device__ inline DecodeItem decode_item(const DecodeParams& p, int64_t i) {
+  DecodeItem it{};
+  int ns = p.n_split_main, nc = p.n_main;
+  it.cls = kMain;
+  if (i >= p.n_items_main) { i -= p.n_items_main; it.cls = kStream; ns = p.n_split_stream; nc = p.n_stream; }
+  it.split = (int)(i % ns);
+  const int64_t bh = i / ns;
+  it.b = (int)(bh / nc);
+  it.rank = (int)(bh % nc);
+  it.kvh = (it.cls == kMain) ? p.main_heads[it.rank] : p.stream_heads[it.rank];
+  return it;
+}
+
+// Number of cache slots holding visible keys for a sequence of length len:
+// every occupied slot is visible to the query at len - 1 (the caches keep
+// exactly the positions the visibility rule needs), so a decode reads slots
+// [0, n) in storage order.
+__host__ __device__ inline int64_t decode_valid_slots(const DecodeParams& p, int cls, int64_t len) {
+  // main: a ring of main_cap slots, or a contiguous cache of main_cap >= len
+  // slots (the clamp keeps a bad length inside the buffer).
+  const int64_t cap = (cls == kStream) ? (int64_t)p.sink + p.recent : p.main_cap;
+  return len < cap ? len : cap;
+}
+
+// Launchers (defined in the .hip files).
+hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_prefill(const PrefillParams& p, int64_t n_blocks, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+
+}  // namespace duo

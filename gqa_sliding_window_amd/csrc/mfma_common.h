@@ -1,0 +1,72 @@
+// gfx950 building blocks shared by the attention kernels: bf16 MFMA tiles,
+// the LDS transpose read, and bf16 packing.
+//
+// MFMA layouts used (v_mfma_f32_16x16x32_bf16, wave64; lane l, r = l % 16,
+// g = l / 16):
+//   A operand (16 x 32):  lane holds A[r][8g .. 8g+7]
+//   B operand (32 x 16):  lane holds B[8g .. 8g+7][r]
+//   C/D       (16 x 16):  lane holds D[4g .. 4g+3][r]
+// Attention is computed transposed, S^T = K Q^T, so that every lane owns one
+// query row (column r) and the row's softmax statistics stay in the lane.
+// The PV product O^T = V^T P^T takes P^T straight from the S^T registers:
+// keys are consumed in the order sigma(8g + j) = 4g + j (j < 4) and
+// 16 + 4g + (j - 4) (j >= 4) of each 32-key block, and V^T is read in that
+// same order with ds_read_b64_tr_b16, which gives lane i of each 16-lane group
+// element i % 4 of the 4-element chunk addressed by lane i / 4 + 4 j.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace duo {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 4 x 16 transpose read: lane i of a 16-lane group gets column (i) of the
+// 4-row block whose rows the group's lanes address (4 lanes per row, 4
+// consecutive bf16 each).
+__device__ __forceinline__ i16x4 lds_read_tr16(const uint16_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+__device__ __forceinline__ bf16x8 cat_bf16(const i16x4& lo, const i16x4& hi) {
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ bf16x8 pack_bf16(const f32x4& lo, const f32x4& hi) {
+  f32x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_convertvector(v, bf16x8);
+}
+
+__device__ __forceinline__ bf16x4 pack_bf16x4(const f32x4& v) {
+  return __builtin_convertvector(v, bf16x4);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_xor_max(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask));
+}
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLn2 = 0.6931471805599453f;
+// Lazy rescaling: the running row maximum is only moved when a new logit
+// exceeds it by more than this many powers of two; until then exponentials may
+// reach 2^8, far inside fp32 and bf16 range. Output and normaliser share the
+// stale maximum, so the result is unchanged.
+constexpr float kRescaleThreshold = 8.0f;
+
+}  // namespace duo

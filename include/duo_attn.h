@@ -1,0 +1,191 @@
+/*
+ * duo_attn.h -- C ABI of the MI355X (gfx950) hybrid GQA attention library:
+ * causal full-attention layers, causal sliding-window layers, and
+ * DuoAttention per-KV-head routing (full-context heads vs. streaming heads
+ * that keep sink + recent tokens in a compacted cache).
+ *
+ * Sources of the method (titles and sections of the pages):
+ *  - Hugging Face model card "DuoAttention Laguna Adapter": "Summary" (KV heads
+ *    split into full-context and streaming heads; sink size 64, recent size
+ *    256; a learned full_attention_heads tensor), "Why It Works" (full-context
+ *    heads retain all prior tokens, streaming heads keep sink tokens plus the
+ *    most recent tokens), "Changes In This Submission" (head reordering so
+ *    full and streaming heads are separated; static Duo KV cache).
+ *  - Blog post on Laguna-M.1-8bit attention: sliding-window section (a token
+ *    attends a fixed window of preceding tokens, O(n^2) -> O(n*w)),
+ *    implementation section (per-layer layer_types / sliding_window, None for
+ *    full layers), mask-generation section (causal and sliding-window causal
+ *    masks chosen per layer type).
+ *  - SGLang cookbook "Laguna-XS-2.1", section 1 "Model Introduction": 48 Q / 8
+ *    KV heads, window 512, 30 sliding + 10 full layers.
+ *
+ * Visibility of key position j for a query at position i (G = Hq / Hkv, query
+ * head h uses KV head h / G):
+ *   full-context head, FULL layer (or window <= 0):  0 <= j <= i
+ *   full-context head, SLIDING layer, window W > 0:  i - W + 1 <= j <= i
+ *   streaming head (any layer):                      j <= i and (j < sink or j > i - recent)
+ *
+ * Conventions for every entry point:
+ *  - All tensors are bfloat16 (16-bit bit patterns), row-major, densely
+ *    packed, head_dim = 128, and 16-byte aligned. Device pointers are owned by
+ *    the caller; the library never allocates, frees or retains them.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream). Calls only
+ *    enqueue work and return; results are visible after the stream is
+ *    synchronised.
+ *  - Validation is synchronous and has no side effects: a non-zero return
+ *    means nothing was launched. duo_last_error() then describes the problem
+ *    (thread-local, valid until the next call on the same thread).
+ *  - Calls on different streams that write the same cache or workspace race.
+ */
+#ifndef DUO_ATTN_H
+#define DUO_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DUO_ATTN_VERSION 1
+#define DUO_HEAD_DIM 128
+#define DUO_MAX_KV_HEADS 32
+#define DUO_MAX_GROUP 16
+
+typedef enum duo_status {
+  DUO_OK = 0,
+  DUO_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or range   */
+  DUO_ERR_UNSUPPORTED = -2,  /* head_dim != 128, group > 16, kv heads > 32     */
+  DUO_ERR_CAPACITY = -3,     /* positions beyond the caller's cache capacity  */
+  DUO_ERR_WORKSPACE = -4,    /* decode workspace missing or too small         */
+  DUO_ERR_HIP = -5           /* a HIP launch failed                          */
+} duo_status;
+
+typedef enum duo_layer_kind {
+  DUO_LAYER_FULL = 0,        /* causal attention over the whole prefix        */
+  DUO_LAYER_SLIDING = 1      /* causal sliding window of `window` positions   */
+} duo_layer_kind;
+
+/* One attention layer (host memory, read only during the call).
+ * `full_attention_heads` is this layer's row of the adapter's learned
+ * full_attention_heads tensor (model card "DuoAttention Laguna Adapter",
+ * "Summary"/"Training"), reduced to a binary mask: nonzero = full-context KV
+ * head. NULL = no Duo routing, every KV head keeps full context.
+ * `window` applies to SLIDING layers only; <= 0 means no window (Laguna-M.1-8bit
+ * blog post, implementation section: sliding_window is None for non-sliding
+ * layers). `scale` 0 means 1/sqrt(head_dim). */
+typedef struct duo_layer {
+  int32_t num_q_heads;       /* Hq (48 for Laguna-XS-2.1)                     */
+  int32_t num_kv_heads;      /* Hkv (8); Hq % Hkv == 0, Hq / Hkv <= 16        */
+  int32_t head_dim;          /* must be 128                                   */
+  int32_t kind;              /* duo_layer_kind                                */
+  int32_t window;            /* 512 on sliding layers                         */
+  int32_t sink;              /* 64: first positions kept by streaming heads   */
+  int32_t recent;            /* 256: newest positions kept by streaming heads */
+  const uint8_t* full_attention_heads; /* host [num_kv_heads] or NULL        */
+  float scale;
+} duo_layer;
+
+/* The static KV cache of one layer (device memory, caller owned).
+ * Heads are split by class; within a class they are numbered by ascending KV
+ * head index ("rank"), the cache-side image of the adapter's head reordering
+ * (model card, "Changes In This Submission"). n_main = number of full-context
+ * KV heads (all Hkv without a mask), n_stream = Hkv - n_main.
+ *   k_main/v_main     [B, n_main, main_capacity, 128]
+ *       FULL layer (or window <= 0): slot = position; main_capacity is the
+ *       largest position count the cache can hold.
+ *       SLIDING layer with window W > 0: a ring, slot = position mod W;
+ *       main_capacity must equal W.
+ *   k_stream/v_stream [B, n_stream, sink + recent, 128]
+ *       slot = position if position < sink,
+ *              else sink + (position - sink) mod recent.
+ * Pointers of an empty class may be NULL. */
+typedef struct duo_kv_cache {
+  void* k_main;
+  void* v_main;
+  int64_t main_capacity;
+  void* k_stream;
+  void* v_stream;
+} duo_kv_cache;
+
+/* Write new K/V rows into the cache (the streaming-head cache manager).
+ * k_new, v_new : device [batch, num_tokens, Hkv, 128] (token-major, as the
+ *                projections emit them); token t of sequence b is position
+ *                start_pos[b] + t.
+ * start_pos    : device int32 [batch], >= 0.
+ * max_end_pos  : host upper bound on max_b(start_pos[b]) + num_tokens; checked
+ *                against main_capacity for contiguous caches (CAPACITY error).
+ *                The kernel also drops any write whose slot would fall outside
+ *                a contiguous cache, so a wrong bound cannot corrupt memory.
+ * When one call brings more positions than a ring holds, only the newest
+ * positions of each slot are written, so every slot has exactly one writer.
+ * Bit copy: no rounding. */
+int duo_kv_append(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch,
+                  const void* k_new, const void* v_new, int32_t num_tokens,
+                  const int32_t* start_pos, int64_t max_end_pos, void* stream);
+
+/* Prefill attention for a chunk of num_tokens query positions
+ * [start_pos, start_pos + num_tokens) of every sequence in the batch.
+ * q   : device [batch, num_tokens, Hq, 128]
+ * k,v : device [batch, num_tokens, Hkv, 128] -- the chunk's own keys/values.
+ * past: the cache holding positions [0, start_pos) as duo_kv_append left it;
+ *       may be NULL when start_pos == 0. The chunk's K/V are read from k/v,
+ *       not from the cache (attend, then append the chunk).
+ * out : device [batch, num_tokens, Hq, 128] bf16 (round to nearest even).
+ * lse : NULL or device float [batch, Hq, num_tokens], natural-log
+ *       log-sum-exp of the scaled logits of each row. */
+int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t batch,
+                     const void* q, const void* k, const void* v, int32_t num_tokens,
+                     int64_t start_pos, void* out, float* lse, void* stream);
+
+/* Decode attention: one query token per sequence at position seq_lens[b]-1,
+ * whose K/V have already been appended (seq_lens counts them).
+ * q         : device [batch, Hq, 128]
+ * seq_lens  : device int32 [batch], each in [1, max_seq_len]; a 0 entry
+ *             yields a zero output row (lse = -inf).
+ * max_seq_len : host bound used to size the split-K grid.
+ * out       : device [batch, Hq, 128] bf16.  lse: NULL or device float [batch, Hq].
+ * workspace : device scratch of at least duo_attn_decode_workspace_bytes()
+ *             bytes, 256-byte aligned, owned by the caller; holds split-K
+ *             partial results between the two kernels of one call. */
+int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch,
+                    const void* q, const int32_t* seq_lens, int64_t max_seq_len,
+                    void* out, float* lse, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Workspace size for duo_attn_decode; 0 on invalid arguments. Host only. */
+size_t duo_attn_decode_workspace_bytes(const duo_layer* layer, int32_t batch,
+                                       int64_t max_seq_len);
+
+/* Bytes of the static cache for `capacity` positions per sequence (model
+ * card, "Changes In This Submission": static Duo KV cache). Host only.
+ * main_bytes/stream_bytes receive the size of ONE of k/v for each class. */
+int duo_kv_cache_bytes(const duo_layer* layer, int32_t batch, int64_t capacity,
+                       int64_t* main_bytes, int64_t* stream_bytes);
+
+/* Head-class plan (host only, no GPU): for each KV head, its class
+ * (1 = streaming, 0 = full context) and its rank within the class. */
+int duo_head_plan(const duo_layer* layer, int32_t* head_class, int32_t* head_rank,
+                  int32_t* n_main, int32_t* n_stream);
+
+/* Prefill work plan (host only): the number of workgroups the prefill launch
+ * uses; when `items` is not NULL it receives, per workgroup, four int32
+ * (batch, q_head, q_tile, key_tiles), or (-1, -1, -1, 0) for padding, with
+ * q_tile a 128-row tile of the chunk and key_tiles the 64-key tiles the
+ * workgroup visits after masked tiles are skipped. */
+int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens,
+                     int64_t start_pos, int32_t* items, int64_t* n_items);
+
+/* Decode work plan (host only): keys per split and number of split-K work
+ * items; when `items` is not NULL it receives per item four int32
+ * (batch, kv_head, split, class). */
+int duo_decode_plan(const duo_layer* layer, int32_t batch, int64_t max_seq_len,
+                    int32_t* split_keys, int32_t* items, int64_t* n_items);
+
+const char* duo_last_error(void);
+int duo_attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DUO_ATTN_H */

@@ -98,6 +98,14 @@ def attend(qvec: np.ndarray, kmat: np.ndarray, vmat: np.ndarray, scale: float):
     return (w @ vmat) / z, m + np.log(z)
 
 
+def _rows(vis: np.ndarray):
+    """Index for the visible rows: a slice when they are consecutive (a view,
+    no copy), else the index array itself. Selects the same rows either way."""
+    if len(vis) and vis[-1] - vis[0] + 1 == len(vis):
+        return slice(int(vis[0]), int(vis[-1]) + 1)
+    return vis
+
+
 def _layer_scale(d: int, scale):
     return 1.0 / np.sqrt(d) if not scale else float(scale)
 
@@ -131,7 +139,8 @@ def prefill_rows(q, k_pos, v_pos, start_pos: int, rows, *, hkv: int, layer: str,
             cache.clear()
             cache[key] = (bf16_bits_to_f64(k_pos[b, :, kvh]), bf16_bits_to_f64(v_pos[b, :, kvh]))
         kf, vf = cache[key]
-        out[n], lse[n] = attend(bf16_bits_to_f64(q[b, t, h]), kf[vis], vf[vis], sc)
+        sel = _rows(vis)
+        out[n], lse[n] = attend(bf16_bits_to_f64(q[b, t, h]), kf[sel], vf[sel], sc)
     return out, lse
 
 

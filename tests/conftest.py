@@ -27,3 +27,12 @@ def lib():
     import gqa_sliding_window_amd as g
     g.load()
     return g
+
+
+def pytest_collection_modifyitems(config, items):
+    if gpu_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU on this host")
+    for item in items:
+        if "gpu" in item.keywords:
+            item.add_marker(skip)

@@ -1,0 +1,206 @@
+"""C-ABI contract on the CPU (no GPU): the library loads, exports every symbol
+include/duo_attn.h declares, rejects bad arguments before any launch, and
+its host-side plans are complete and skip masked tiles."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import gqa_sliding_window_amd as g
+from gqa_sliding_window_amd import Layer, FULL, SLIDING
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "duo_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(duo_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 10
+    raw = ctypes.CDLL(g.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+    assert lib.load().duo_attn_version() == 1
+
+
+def _err(fn, *a, **k):
+    with pytest.raises(g.DuoError) as e:
+        fn(*a, **k)
+    return e.value.code
+
+
+class FakeTensor:
+    """Host stand-in carrying a pointer and a shape (validation only; the
+    calls below fail before anything reaches the GPU)."""
+    def __init__(self, shape, ptr=0x100000):
+        self.shape = shape
+        self._p = ptr
+
+    def data_ptr(self):
+        return self._p
+
+    def numel(self):
+        return int(np.prod(self.shape))
+
+    def element_size(self):
+        return 4
+
+
+def test_layer_validation_errors(lib):
+    q = FakeTensor((1, 8, 48, 128))
+    kv = FakeTensor((1, 8, 8, 128))
+    o = FakeTensor((1, 8, 48, 128))
+    assert _err(g.attn_prefill, Layer(head_dim=64), q, kv, kv, o, stream=0) == -2
+    assert _err(g.attn_prefill, Layer(num_q_heads=47), q, kv, kv, o, stream=0) == -1
+    assert _err(g.attn_prefill, Layer(num_q_heads=34 * 2, num_kv_heads=34), q, kv, kv, o, stream=0) == -2
+    assert _err(g.attn_prefill, Layer(num_q_heads=17, num_kv_heads=1), q, kv, kv, o, stream=0) == -2
+    assert _err(g.attn_prefill, Layer(kind=7), q, kv, kv, o, stream=0) == -1
+    assert _err(g.attn_prefill, Layer(sink=-1), q, kv, kv, o, stream=0) == -1
+    assert _err(g.attn_prefill, Layer(full_attention_heads=[0] * 8, recent=0), q, kv, kv, o, stream=0) == -1
+    assert _err(g.attn_prefill, Layer(scale=float("inf")), q, kv, kv, o, stream=0) == -1
+    assert _err(g.attn_prefill, Layer(scale=-1.0), q, kv, kv, o, stream=0) == -1
+    # misaligned and null pointers
+    assert _err(g.attn_prefill, Layer(), FakeTensor(q.shape, 0x100002), kv, kv, o, stream=0) == -1
+    assert _err(g.attn_prefill, Layer(), FakeTensor(q.shape, 0), kv, kv, o, stream=0) == -1
+    # start_pos > 0 without the past cache
+    assert _err(g.attn_prefill, Layer(), q, kv, kv, o, start_pos=5, stream=0) == -1
+    assert "past cache" in lib.load().duo_last_error().decode()
+
+
+class FakeCache:
+    def __init__(self, k_main=0x200000, v_main=0x300000, cap=1024, k_stream=0x400000, v_stream=0x500000):
+        self.vals = (k_main, v_main, cap, k_stream, v_stream)
+
+    def _c(self, batch_offset=0):
+        return g._Cache(*self.vals)
+
+
+def test_cache_validation_errors(lib):
+    kv = FakeTensor((2, 16, 8, 128))
+    sp = FakeTensor((2,))
+    L = Layer()
+    # capacity exceeded for a contiguous cache
+    assert _err(g.kv_append, L, FakeCache(cap=100), kv, kv, sp, max_end_pos=200, stream=0) == -3
+    # sliding ring must have capacity == window
+    assert _err(g.kv_append, Layer(kind=SLIDING, window=512), FakeCache(cap=500), kv, kv, sp,
+                max_end_pos=16, stream=0) == -1
+    # streaming heads need the stream cache
+    assert _err(g.kv_append, Layer(full_attention_heads=[1, 0, 0, 0, 0, 0, 0, 0]),
+                FakeCache(k_stream=0, v_stream=0), kv, kv, sp, max_end_pos=16, stream=0) == -1
+    # misaligned cache
+    assert _err(g.kv_append, L, FakeCache(k_main=0x200008), kv, kv, sp, max_end_pos=16, stream=0) == -1
+    # max_end_pos below the chunk length
+    assert _err(g.kv_append, L, FakeCache(), kv, kv, sp, max_end_pos=3, stream=0) == -1
+    # prefill start_pos beyond capacity
+    q = FakeTensor((2, 16, 48, 128))
+    assert _err(g.attn_prefill, L, q, kv, kv, q, start_pos=2000, past=FakeCache(cap=1024), stream=0) == -3
+
+
+def test_decode_validation_errors(lib):
+    q = FakeTensor((4, 48, 128))
+    sl = FakeTensor((4,))
+    L = Layer()
+    need = g.decode_workspace_bytes(L, 4, 1000)
+    assert need > 0
+    ws_small = FakeTensor((need // 4 - 1,), 0x600000)
+    assert _err(g.attn_decode, L, FakeCache(cap=1000), q, sl, 1000, q, ws_small, stream=0) == -4
+    ws_mis = FakeTensor((need // 4 + 64,), 0x600010)
+    assert _err(g.attn_decode, L, FakeCache(cap=1000), q, sl, 1000, q, ws_mis, stream=0) == -4
+    ws = FakeTensor((need // 4,), 0x600000)
+    assert _err(g.attn_decode, L, FakeCache(cap=999), q, sl, 1000, q, ws, stream=0) == -3
+    assert _err(g.attn_decode, L, FakeCache(cap=1000), q, sl, 0, q, ws, stream=0) == -1
+    assert g.decode_workspace_bytes(Layer(head_dim=64), 4, 1000) == 0
+
+
+def test_empty_calls_are_noops(lib):
+    kv = FakeTensor((0, 16, 8, 128))
+    g.kv_append(Layer(), FakeCache(), kv, kv, FakeTensor((0,)), max_end_pos=16, stream=0)
+    q = FakeTensor((2, 0, 48, 128))
+    g.attn_prefill(Layer(), q, q, q, q, stream=0)
+
+
+def test_head_plan(lib):
+    cls, rank, nm, ns = g.head_plan(Layer(full_attention_heads=[0, 1, 1, 0, 0, 1, 0, 0]))
+    assert cls == [1, 0, 0, 1, 1, 0, 1, 1]
+    assert rank == [0, 0, 1, 1, 2, 2, 3, 4]
+    assert (nm, ns) == (3, 5)
+    cls, rank, nm, ns = g.head_plan(Layer())
+    assert cls == [0] * 8 and rank == list(range(8)) and (nm, ns) == (8, 0)
+
+
+def test_cache_bytes(lib):
+    L = Layer(full_attention_heads=[1, 0, 0, 0, 0, 0, 0, 0])
+    m, s = g.kv_cache_bytes(L, 16, 131072)
+    assert m == 16 * 1 * 131072 * 256 and s == 16 * 7 * 320 * 256
+    m, s = g.kv_cache_bytes(Layer(kind=SLIDING, window=512), 64, 10 ** 6)
+    assert m == 64 * 8 * 512 * 256 and s == 0
+
+
+def _expected_tiles(layer, qa, qb, streaming):
+    def tiles(lo, hi):
+        return hi // 64 - lo // 64 + 1
+    if not streaming:
+        lo = max(0, qa - layer.window + 1) if layer.main_ring else 0
+        return tiles(lo, qb)
+    n = 0
+    if layer.sink > 0:
+        n += tiles(0, min(qb, layer.sink - 1))
+    lo = max(layer.sink, qa - layer.recent + 1)
+    if lo <= qb:
+        n += tiles(lo, qb)
+    return n
+
+
+@pytest.mark.parametrize("case", [
+    dict(layer=Layer(), B=2, T=1000, P=0),
+    dict(layer=Layer(kind=SLIDING, window=512, num_q_heads=12, num_kv_heads=2), B=1, T=1024, P=0),
+    dict(layer=Layer(full_attention_heads=[0, 0, 0, 0, 1, 0, 1, 0]), B=1, T=8192, P=16384),
+    dict(layer=Layer(full_attention_heads=[0] * 8), B=3, T=77, P=5),
+])
+def test_prefill_plan_covers_every_tile_once_and_skips_masked(lib, case):
+    L, B, T, P = case["layer"], case["B"], case["T"], case["P"]
+    items = g.prefill_plan(L, B, T, P)
+    real = items[items[:, 0] >= 0]
+    nqt = (T + 127) // 128
+    assert len(real) == B * L.num_q_heads * nqt
+    assert len({tuple(r[:3]) for r in real}) == len(real)
+    G = L.num_q_heads // L.num_kv_heads
+    mask = L.full_attention_heads
+    for b, h, qt, nt in real:
+        qa = P + 128 * qt
+        qb = min(qa + 127, P + T - 1)
+        streaming = mask is not None and mask[h // G] == 0
+        assert nt == _expected_tiles(L, qa, qb, streaming)
+    # heaviest-first per XCD: along each XCD's sequence the key-tile count never increases
+    # within the main class
+    for x in range(8):
+        seq = [int(r[3]) for r in items[x::8] if r[0] >= 0]
+        if mask is None and L.kind == FULL:
+            assert all(a >= b for a, b in zip(seq, seq[1:]))
+
+
+def test_decode_plan(lib):
+    sk, items = g.decode_plan(Layer(kind=SLIDING, window=512), 64, 32768)
+    assert sk >= 128 and sk % 32 == 0
+    assert len(items) == 64 * 8 * ((512 + sk - 1) // sk)
+    L = Layer(full_attention_heads=[1, 0, 0, 0, 0, 0, 0, 0])
+    sk, items = g.decode_plan(L, 16, 131072)
+    full = items[items[:, 3] == 0]
+    stream = items[items[:, 3] == 1]
+    assert len(full) == 16 * ((131072 + sk - 1) // sk)
+    assert len(stream) == 16 * 7 * ((320 + sk - 1) // sk)
+    assert set(full[:, 1].tolist()) == {0} and set(stream[:, 1].tolist()) == set(range(1, 8))
+    assert (items[:, 3][:len(full)] == 0).all()   # main-class (long) items come first
+
+
+def test_visible_pairs_closed_forms():
+    L = Layer(kind=SLIDING, window=512, num_q_heads=12, num_kv_heads=2)
+    assert g.prefill_flops(L, 1, 1024) == 2417491968
+    assert g.prefill_flops(Layer(), 4, 8192) == 3298937536512
