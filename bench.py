@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Benchmark of the hybrid GQA / sliding-window / DuoAttention attention path
+on one MI355X.
+
+Headline (`value`): prefill TFLOP/s of the full-attention prefill workload
+(batch 4, 48 query / 8 KV heads, head_dim 128, 8192 causal tokens, bf16 in,
+fp32 accumulate). One step = one duo_attn_prefill call over the whole batch.
+Algorithmic FLOP = 4 * 128 per (query row, visible key) pair; masked pairs
+are not counted.
+
+The same JSON line carries the other halves of the metric, each timed the
+same way (HIP events on the stream the kernels run on, inputs resident in
+HBM):
+  decode      -- KV GB/s of the sliding-window decode (batch 64, window-512
+                 ring) and of the DuoAttention decode (batch 16, contexts up to
+                 131072, Bernoulli(0.25) full-head mask); algorithmic bytes =
+                 every visible K and V row read once per KV head; several cache
+                 replicas are rotated so the 256 MB Infinity Cache cannot serve
+                 them;
+  chunked_prefill -- DuoAttention prefill of 131072 tokens in 8192-token
+                 chunks (attend + append per chunk);
+  kv_append   -- the cache manager on one 8192-token chunk.
+`roofline` describes the dominant kernel (the prefill kernel). `cpu_baseline`
+times the float64 oracle on a bounded sample of the headline workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = "prefill TFLOP/s (% MFMA peak) + decode KV GB/s (% HBM peak), 48Q/8KV d128"
+PEAK_MFMA_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+HERE = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Timer:
+    """HIP-event timing on torch's current stream (the stream the library
+    launches on)."""
+
+    def __init__(self, torch):
+        self.torch = torch
+
+    def run(self, fn, warmup, steps):
+        torch = self.torch
+        for i in range(warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        s = torch.cuda.current_stream()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for i in range(steps):
+            fn(warmup + i)
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per call
+
+
+def dev_bits(torch, bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def bench_prefill(torch, G, wl, timer, warmup, steps):
+    w = wl.WORKLOADS[2]
+    log(f"prefill workload {w.name}: generating inputs")
+    q = wl.normal_tokens(w.seed, wl.Q, w.batch, 0, w.seq, w.hq, 128)
+    k = wl.normal_tokens(w.seed, wl.K, w.batch, 0, w.seq, w.hkv, 128)
+    v = wl.normal_tokens(w.seed, wl.V, w.batch, 0, w.seq, w.hkv, 128)
+    qd, kd, vd = dev_bits(torch, q), dev_bits(torch, k), dev_bits(torch, v)
+    out = torch.empty_like(qd)
+    layer = G.Layer()
+    flops = G.prefill_flops(layer, w.batch, w.seq)
+    log("prefill: timing")
+    ms = timer.run(lambda i: G.attn_prefill(layer, qd, kd, vd, out), warmup, steps)
+    return w, (q, k, v), flops, ms
+
+
+def bench_decode_sliding(torch, G, wl, timer, warmup, steps, replicas=8):
+    w = wl.WORKLOADS[3]
+    layer = G.Layer(kind=G.SLIDING, window=w.window)
+    L = wl.context_lengths(w)
+    log(f"decode workload {w.name}: filling {replicas} ring replicas")
+    lows = np.maximum(0, L - w.window)
+    ks = wl.normal_tokens_ragged(w.seed, wl.K, lows.tolist(), (L - lows).tolist(), w.hkv, 128)
+    vs = wl.normal_tokens_ragged(w.seed, wl.V, lows.tolist(), (L - lows).tolist(), w.hkv, 128)
+    kb = dev_bits(torch, np.stack(ks))
+    vb = dev_bits(torch, np.stack(vs))
+    caches = []
+    sp = torch.tensor(lows, dtype=torch.int32, device="cuda")
+    for r in range(replicas):
+        c = G.KVCache(layer, w.batch, w.window, zero=False)
+        G.kv_append(layer, c, kb, vb, sp, max_end_pos=int(L.max()))
+        caches.append(c)
+    q = dev_bits(torch, wl.decode_queries(w.seed, w.batch, w.hq, 128))
+    out = torch.empty_like(q)
+    sl = torch.tensor(L, dtype=torch.int32, device="cuda")
+    maxlen = int(L.max())
+    ws = torch.empty(G.decode_workspace_bytes(layer, w.batch, maxlen) // 4 + 64, dtype=torch.float32, device="cuda")
+    nbytes = int(sum(min(int(x), w.window) for x in L)) * w.hkv * 128 * 2 * 2
+    log("decode sliding: timing")
+    ms = timer.run(lambda i: G.attn_decode(layer, caches[i % replicas], q, sl, maxlen, out, ws), warmup, steps)
+    return w, nbytes, ms, replicas
+
+
+def bench_decode_duo(torch, G, wl, timer, warmup, steps, replicas=2):
+    w = wl.WORKLOADS[4]
+    mask = wl.duo_mask(w).tolist()
+    layer = G.Layer(full_attention_heads=mask)
+    L = wl.context_lengths(w)
+    log(f"decode workload {w.name}: mask {mask}, filling {replicas} cache replicas")
+    gen = torch.Generator(device="cuda")
+    chunk = 16384
+    caches = [G.KVCache(layer, w.batch, w.len_hi, zero=False) for _ in range(replicas)]
+    for b in range(w.batch):
+        for p in range(0, int(L[b]), chunk):
+            T = min(chunk, int(L[b]) - p)
+            gen.manual_seed(w.seed * 1000003 + b * 1009 + p)
+            kc = torch.randn((1, T, w.hkv, 128), generator=gen, device="cuda").to(torch.bfloat16)
+            vc = torch.randn((1, T, w.hkv, 128), generator=gen, device="cuda").to(torch.bfloat16)
+            sp = torch.tensor([p], dtype=torch.int32, device="cuda")
+            for c in caches:
+                G.kv_append(layer, c, kc, vc, sp, max_end_pos=p + T, batch=1, batch_offset=b)
+    q = dev_bits(torch, wl.decode_queries(w.seed, w.batch, w.hq, 128))
+    out = torch.empty_like(q)
+    sl = torch.tensor(L, dtype=torch.int32, device="cuda")
+    ws = torch.empty(G.decode_workspace_bytes(layer, w.batch, w.len_hi) // 4 + 64, dtype=torch.float32, device="cuda")
+    nf = sum(1 for m in mask if m)
+    ns = w.hkv - nf
+    sr = w.sink + w.recent
+    nbytes = int(sum(nf * int(x) + ns * min(int(x), sr) for x in L)) * 128 * 2 * 2
+    log("decode duo: timing")
+    ms = timer.run(lambda i: G.attn_decode(layer, caches[i % replicas], q, sl, w.len_hi, out, ws), warmup, steps)
+    return w, nbytes, ms, replicas, mask, int(L.sum())
+
+
+def bench_chunked(torch, G, wl, timer, warmup, steps):
+    w = wl.WORKLOADS[5]
+    mask = wl.duo_mask(w).tolist()
+    layer = G.Layer(full_attention_heads=mask)
+    log(f"chunked prefill workload {w.name}: mask {mask}, generating inputs on the GPU")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(w.seed)
+    n_chunks = w.seq // w.chunk
+    q = torch.randn((n_chunks, 1, w.chunk, w.hq, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn((n_chunks, 1, w.chunk, w.hkv, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn((n_chunks, 1, w.chunk, w.hkv, 128), generator=gen, device="cuda").to(torch.bfloat16)
+    out = torch.empty((n_chunks, 1, w.chunk, w.hq, 128), dtype=torch.bfloat16, device="cuda")
+    cache = G.KVCache(layer, 1, w.seq, zero=False)
+    starts = [torch.tensor([c * w.chunk], dtype=torch.int32, device="cuda") for c in range(n_chunks)]
+    flops = sum(G.prefill_flops(layer, 1, w.chunk, c * w.chunk) for c in range(n_chunks))
+
+    def one_pass(_):
+        for c in range(n_chunks):
+            G.attn_prefill(layer, q[c], k[c], v[c], out[c], start_pos=c * w.chunk, past=cache)
+            G.kv_append(layer, cache, k[c], v[c], starts[c], max_end_pos=(c + 1) * w.chunk)
+
+    log("chunked prefill: timing passes")
+    ms = timer.run(one_pass, warmup, steps)
+    # attention-only: per-chunk prefill calls alone, cache already filled
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_chunks)]
+    torch.cuda.synchronize()
+    for c in range(n_chunks):
+        ev[2 * c].record(s)
+        G.attn_prefill(layer, q[c], k[c], v[c], out[c], start_pos=c * w.chunk, past=cache)
+        ev[2 * c + 1].record(s)
+    torch.cuda.synchronize()
+    attn_ms = sum(ev[2 * c].elapsed_time(ev[2 * c + 1]) for c in range(n_chunks))
+    # cache manager on one chunk: read 2 x chunk rows, write 2 x chunk rows
+    app_ms = timer.run(lambda i: G.kv_append(layer, cache, k[0], v[0], starts[0], max_end_pos=w.chunk), 2, 20)
+    app_bytes = 2 * 2 * w.chunk * w.hkv * 128 * 2
+    return w, mask, flops, ms, attn_ms, app_ms, app_bytes
+
+
+def cpu_baseline(w, qkv, target_s):
+    """Time the float64 oracle on a bounded sample of the headline workload."""
+    import threadpoolctl
+    import oracle
+    import workloads as wl
+    q, k, v = qkv
+    rows = wl.sample_query_rows(w, w.seq, 4096)
+    rng = np.random.default_rng(0)
+    rows = rows[rng.permutation(len(rows))]
+    done = 0
+    flops = 0
+    t0 = time.perf_counter()
+    with threadpoolctl.threadpool_limits(1):
+        while done < len(rows) and time.perf_counter() - t0 < target_s:
+            batch = rows[done:done + 64]
+            batch = batch[np.lexsort((batch[:, 2], batch[:, 1], batch[:, 0]))]
+            oracle.prefill_rows(q, k, v, 0, batch, hkv=w.hkv, layer="full")
+            flops += int(4 * 128 * (batch[:, 2] + 1).sum())
+            done += len(batch)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} seeded query rows of the headline workload (float64, one thread), "
+                      f"{dt:.1f} s", "rows_per_s": done / dt}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sections", default="prefill,decode,chunked",
+                    help="comma list of prefill, decode, chunked")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 = skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this path runs without sharding or collectives; "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gqa_sliding_window_amd as G
+    import workloads as wl
+    G.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    timer = Timer(torch)
+    sections = set(args.sections.split(","))
+    res = {"metric": METRIC, "value": None, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16)"}
+
+    w2 = qkv = None
+    if "prefill" in sections:
+        w2, qkv, flops, ms = bench_prefill(torch, G, wl, timer, args.warmup, args.steps)
+        tflops = flops / (ms * 1e-3) / 1e12
+        res["value"] = tflops
+        res["ms_per_step"] = ms
+        res["config"] = {"workload": w2.name, "batch": w2.batch, "seq_len": w2.seq, "q_heads": w2.hq,
+                         "kv_heads": w2.hkv, "head_dim": 128, "layer": "full causal",
+                         "algorithmic_flop_per_step": flops}
+        traffic = None
+        if os.path.exists(TRAFFIC_FILE):
+            t = json.load(open(TRAFFIC_FILE)).get("prefill_kernel")
+            if t and t.get("workload") == w2.name:
+                traffic = t.get("bytes_per_launch")
+        res["roofline"] = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": tflops,
+                           "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": tflops / PEAK_MFMA_BF16_TFLOPS, "traffic": traffic}
+        log(f"prefill: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
+
+    if "decode" in sections:
+        d = {}
+        w3, nb3, ms3, rep3 = bench_decode_sliding(torch, G, wl, timer, args.warmup, args.steps)
+        gbs3 = nb3 / (ms3 * 1e-3) / 1e9
+        d["sliding_window"] = {"workload": w3.name, "kv_bytes": nb3, "ms": ms3, "GB/s": gbs3,
+                               "frac_hbm_peak": gbs3 / PEAK_HBM_GBS, "cache_replicas": rep3}
+        log(f"decode sliding: {ms3 * 1e3:.1f} us, {gbs3:.0f} GB/s")
+        w4, nb4, ms4, rep4, mask4, sumL = bench_decode_duo(torch, G, wl, timer, args.warmup, args.steps)
+        gbs4 = nb4 / (ms4 * 1e-3) / 1e9
+        d["duo"] = {"workload": w4.name, "mask": mask4, "sum_context": sumL, "kv_bytes": nb4, "ms": ms4,
+                    "GB/s": gbs4, "frac_hbm_peak": gbs4 / PEAK_HBM_GBS, "cache_replicas": rep4}
+        log(f"decode duo: {ms4 * 1e3:.1f} us, {gbs4:.0f} GB/s")
+        res["decode"] = d
+
+    if "chunked" in sections:
+        w5, mask5, fl5, ms5, attn5, app_ms, app_bytes = bench_chunked(torch, G, wl, timer, 1, max(1, args.steps // 10))
+        res["chunked_prefill"] = {"workload": w5.name, "mask": mask5, "algorithmic_flop": fl5,
+                                  "ms_total": ms5, "TFLOP/s": fl5 / (ms5 * 1e-3) / 1e12,
+                                  "attention_only_ms": attn5,
+                                  "attention_only_TFLOP/s": fl5 / (attn5 * 1e-3) / 1e12}
+        res["kv_append"] = {"workload": "one 8192-token chunk, 8 KV heads", "ms": app_ms,
+                            "GB/s": app_bytes / (app_ms * 1e-3) / 1e9}
+        log(f"chunked prefill: {ms5:.2f} ms total, attention {attn5:.2f} ms")
+
+    if w2 is not None and args.cpu_seconds > 0:
+        log("cpu baseline: timing the oracle")
+        res["cpu_baseline"] = cpu_baseline(w2, qkv, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

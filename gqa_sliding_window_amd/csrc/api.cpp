@@ -106,11 +106,6 @@ int check_cache(const Layer& L, const duo_kv_cache* c, bool need_main, bool need
   return DUO_OK;
 }
 
-void fill_heads(const Layer& L, int8_t* main_heads, int8_t* stream_heads) {
-  std::memcpy(main_heads, L.plan.main_heads, kMaxKv);
-  std::memcpy(stream_heads, L.plan.stream_heads, kMaxKv);
-}
-
 int hip_status(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(DUO_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return ok();
@@ -140,7 +135,6 @@ int build_prefill(const Layer& L, int32_t batch, int32_t T, int64_t start_pos, P
   p->n_units_main = (int32_t)um;
   p->n_units = (int32_t)(um + us);
   p->scale_log2 = L.scale * 1.4426950408889634f;
-  fill_heads(L, p->main_heads, p->stream_heads);
   const int64_t units8 = (p->n_units + kXcds - 1) / kXcds * kXcds;
   *n_blocks = units8 * L.group;
   if (*n_blocks > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "prefill grid too large");
@@ -164,7 +158,6 @@ int build_decode(const Layer& L, int32_t batch, int64_t max_seq_len, int64_t mai
   p->n_stream = L.plan.n_stream;
   p->stream_mask = L.plan.stream_mask;
   p->scale_log2 = L.scale * 1.4426950408889634f;
-  fill_heads(L, p->main_heads, p->stream_heads);
   const int64_t keys_main = L.main_ring ? (max_seq_len < L.window ? max_seq_len : L.window) : max_seq_len;
   const int64_t sr = (int64_t)L.sink + L.recent;
   const int64_t keys_stream = max_seq_len < sr ? max_seq_len : sr;

@@ -24,6 +24,21 @@ namespace duo {
 
 constexpr int kDPitch = kD + 8;
 
+// One 32-key tile, global -> registers: rows ld_row + 4 j (clamped to the
+// split's last slot), 16-byte chunk ld_chunk; each load instruction of the
+// wave covers 4 consecutive 256-byte rows.
+__device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t* vbase, int64_t k0,
+                                          int64_t k_end, int ld_row, int ld_chunk, u32x4 (&stK)[8],
+                                          u32x4 (&stV)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int64_t slot = k0 + ld_row + 4 * j;
+    slot = slot < k_end ? slot : k_end - 1;
+    stK[j] = *reinterpret_cast<const u32x4*>(kbase + slot * kD + ld_chunk * 8);
+    stV[j] = *reinterpret_cast<const u32x4*>(vbase + slot * kD + ld_chunk * 8);
+  }
+}
+
 __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[kDecodeKeys * kDPitch];
   __shared__ __attribute__((aligned(16))) uint16_t sV[kDecodeKeys * kDPitch];
@@ -59,7 +74,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     const uint16_t* src = p.q + ((int64_t)it.b * p.hq + it.kvh * p.group + (ok ? r16 : 0)) * kD + 8 * g;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
-      uint4 raw = ok ? *reinterpret_cast<const uint4*>(src + 32 * ds) : make_uint4(0, 0, 0, 0);
+      u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(src + 32 * ds) : u32x4{0u, 0u, 0u, 0u};
       qf[ds] = __builtin_bit_cast(bf16x8, raw);
     }
   }
@@ -67,16 +82,7 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   // staging: rows (lane / 16) + 4 j, chunk lane % 16
   const int ld_row = lane >> 4;
   const int ld_chunk = lane & 15;
-  uint4 stK[8], stV[8];
-  auto load_tile = [&](int64_t k0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int64_t slot = k0 + ld_row + 4 * j;
-      slot = slot < k_end ? slot : k_end - 1;
-      stK[j] = *reinterpret_cast<const uint4*>(kbase + slot * kD + ld_chunk * 8);
-      stV[j] = *reinterpret_cast<const uint4*>(vbase + slot * kD + ld_chunk * 8);
-    }
-  };
+  u32x4 stK[8], stV[8];
 
   const float c = p.scale_log2;
   float m = kNegInf, l = 0.f;
@@ -84,17 +90,17 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_tile(k_begin);
+  load_tile(kbase, vbase, k_begin, k_end, ld_row, ld_chunk, stK, stV);
   for (int64_t k0 = k_begin; k0 < k_end; k0 += kDecodeKeys) {
     __syncthreads();  // previous tile's LDS reads are done
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int off = (ld_row + 4 * j) * kDPitch + ld_chunk * 8;
-      *reinterpret_cast<uint4*>(&sK[off]) = stK[j];
-      *reinterpret_cast<uint4*>(&sV[off]) = stV[j];
+      *reinterpret_cast<u32x4*>(&sK[off]) = stK[j];
+      *reinterpret_cast<u32x4*>(&sV[off]) = stV[j];
     }
     __syncthreads();
-    if (k0 + kDecodeKeys < k_end) load_tile(k0 + kDecodeKeys);
+    if (k0 + kDecodeKeys < k_end) load_tile(kbase, vbase, k0 + kDecodeKeys, k_end, ld_row, ld_chunk, stK, stV);
 
     f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll

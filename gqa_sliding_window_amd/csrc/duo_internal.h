@@ -32,6 +32,29 @@ struct HeadPlan {
   int8_t stream_heads[kMaxKv];
 };
 
+// Index of the n-th set bit of mask (n counted from 0); -1 if there is none.
+// Used instead of rank -> head tables so that kernels never index their
+// by-value parameter block at run time (which would copy it to scratch).
+__host__ __device__ inline int nth_set_bit(uint32_t mask, int n) {
+  for (int b = 0; b < 32; ++b) {
+    if ((mask >> b) & 1u) {
+      if (n == 0) return b;
+      --n;
+    }
+  }
+  return -1;
+}
+
+__host__ __device__ inline uint32_t all_heads_mask(int hkv) {
+  return hkv >= 32 ? 0xFFFFFFFFu : ((1u << hkv) - 1u);
+}
+
+// kv head of the given class and rank
+__host__ __device__ inline int class_head(uint32_t stream_mask, int hkv, int cls, int rank) {
+  const uint32_t m = cls ? stream_mask : (all_heads_mask(hkv) & ~stream_mask);
+  return nth_set_bit(m, rank);
+}
+
 __host__ __device__ inline int head_rank(uint32_t stream_mask, int kvh) {
   const uint32_t below = (kvh == 0) ? 0u : (0xFFFFFFFFu >> (32 - kvh));
   const bool s = (stream_mask >> kvh) & 1u;
@@ -78,8 +101,6 @@ struct PrefillParams {
   int32_t n_units_main;  // (q tile, batch, main head) units
   int32_t n_units;       // all units
   float scale_log2;      // scale * log2(e)
-  int8_t main_heads[kMaxKv];
-  int8_t stream_heads[kMaxKv];
 };
 
 struct PrefillItem {
@@ -111,7 +132,7 @@ __host__ __device__ inline PrefillItem prefill_item(const PrefillParams& p, int6
   const int64_t grp = u % groups;
   it.b = (int)(grp / n_class);
   it.rank = (int)(grp % n_class);
-  it.kvh = (it.cls == kMain) ? p.main_heads[it.rank] : p.stream_heads[it.rank];
+  it.kvh = class_head(p.stream_mask, p.hkv, it.cls, it.rank);
   it.qhead = it.kvh * p.group + g;
   return it;
 }
@@ -169,8 +190,6 @@ struct DecodeParams {
   int32_t n_split_main, n_split_stream, n_split_max;
   int32_t n_items_main, n_items;
   float scale_log2;
-  int8_t main_heads[kMaxKv];
-  int8_t stream_heads[kMaxKv];
 };
 
 struct DecodeItem { int32_t cls, b, rank, kvh, split; };
@@ -186,7 +205,7 @@ __host__ __device__ inline DecodeItem decode_item(const DecodeParams& p, int64_t
   const int64_t bh = i / ns;
   it.b = (int)(bh / nc);
   it.rank = (int)(bh % nc);
-  it.kvh = (it.cls == kMain) ? p.main_heads[it.rank] : p.stream_heads[it.rank];
+  it.kvh = class_head(p.stream_mask, p.hkv, it.cls, it.rank);
   return it;
 }
 

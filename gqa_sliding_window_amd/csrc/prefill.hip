@@ -55,6 +55,42 @@ __device__ __forceinline__ RowSrc key_row(const PrefillParams& p, const PrefillI
   return r;
 }
 
+// Tile idx of the (at most two) key ranges: its range and first position.
+__device__ __forceinline__ void tile_of(const KeyRange (&rg)[2], int64_t nt0, int64_t idx, KeyRange& r,
+                                        int64_t& lo) {
+  const bool first = idx < nt0;
+  r = first ? rg[0] : rg[1];
+  lo = (r.lo / kPrefillKeys + (first ? idx : idx - nt0)) * kPrefillKeys;
+}
+
+// Global -> registers: rows ld_row + 16 j of the tile; positions outside the
+// range are clamped onto it (their logits are masked, their values finite).
+__device__ __forceinline__ void load_tile(const PrefillParams& p, const PrefillItem& it,
+                                          const KeyRange (&rg)[2], int64_t nt0, int64_t idx, int ld_row,
+                                          int ld_chunk, u32x4 (&stK)[4], u32x4 (&stV)[4]) {
+  KeyRange r;
+  int64_t lo;
+  tile_of(rg, nt0, idx, r, lo);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    int64_t pos = lo + ld_row + 16 * j;
+    pos = pos < r.lo ? r.lo : (pos > r.hi ? r.hi : pos);
+    const RowSrc src = key_row(p, it, pos);
+    stK[j] = *reinterpret_cast<const u32x4*>(src.k + ld_chunk * 8);
+    stV[j] = *reinterpret_cast<const u32x4*>(src.v + ld_chunk * 8);
+  }
+}
+
+__device__ __forceinline__ void store_tile(uint16_t* sk, uint16_t* sv, int ld_row, int ld_chunk,
+                                           const u32x4 (&stK)[4], const u32x4 (&stV)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int off = (ld_row + 16 * j) * kPitch + ld_chunk * 8;
+    *reinterpret_cast<u32x4*>(sk + off) = stK[j];
+    *reinterpret_cast<u32x4*>(sv + off) = stV[j];
+  }
+}
+
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kPrefillKeys * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][kPrefillKeys * kPitch];
@@ -85,7 +121,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     const uint16_t* src = p.q + (((int64_t)it.b * p.T + (ok ? qpos - P0 : 0)) * p.hq + it.qhead) * kD + 8 * g;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
-      uint4 raw = ok ? *reinterpret_cast<const uint4*>(src + 32 * ds) : make_uint4(0, 0, 0, 0);
+      u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(src + 32 * ds) : u32x4{0u, 0u, 0u, 0u};
       qf[t][ds] = __builtin_bit_cast(bf16x8, raw);
     }
   }
@@ -98,32 +134,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   // ---- per-thread staging of one K/V tile: rows (tid/16) + 16 j, 16-byte chunk tid%16
   const int ld_row = tid >> 4;
   const int ld_chunk = tid & 15;
-  uint4 stK[4], stV[4];
-
-  auto tile_of = [&](int64_t idx, int& ri, int64_t& lo) {
-    if (idx < nt0) { ri = 0; lo = (rg[0].lo / kPrefillKeys + idx) * kPrefillKeys; }
-    else { ri = 1; lo = (rg[1].lo / kPrefillKeys + (idx - nt0)) * kPrefillKeys; }
-  };
-  auto load_tile = [&](int64_t idx) {
-    int ri; int64_t lo;
-    tile_of(idx, ri, lo);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      int64_t pos = lo + ld_row + 16 * j;
-      pos = pos < rg[ri].lo ? rg[ri].lo : (pos > rg[ri].hi ? rg[ri].hi : pos);
-      const RowSrc src = key_row(p, it, pos);
-      stK[j] = *reinterpret_cast<const uint4*>(src.k + ld_chunk * 8);
-      stV[j] = *reinterpret_cast<const uint4*>(src.v + ld_chunk * 8);
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int off = (ld_row + 16 * j) * kPitch + ld_chunk * 8;
-      *reinterpret_cast<uint4*>(&sK[buf][off]) = stK[j];
-      *reinterpret_cast<uint4*>(&sV[buf][off]) = stV[j];
-    }
-  };
+  u32x4 stK[4], stV[4];
 
   // ---- running state (log2 domain: x = s * scale * log2 e)
   const float c = p.scale_log2;
@@ -135,17 +146,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_tile(0);
-  store_tile(0);
+  load_tile(p, it, rg, nt0, 0, ld_row, ld_chunk, stK, stV);
+  store_tile(sK[0], sV[0], ld_row, ld_chunk, stK, stV);
   __syncthreads();
 
   for (int64_t idx = 0; idx < ntiles; ++idx) {
     const int buf = (int)(idx & 1);
-    if (idx + 1 < ntiles) load_tile(idx + 1);
+    if (idx + 1 < ntiles) load_tile(p, it, rg, nt0, idx + 1, ld_row, ld_chunk, stK, stV);
 
-    int ri; int64_t lo;
-    tile_of(idx, ri, lo);
-    const KeyRange r = rg[ri];
+    KeyRange r;
+    int64_t lo;
+    tile_of(rg, nt0, idx, r, lo);
     const int64_t hi = lo + kPrefillKeys - 1;
     const bool invisible = !wave_active || lo > qw1 || (r.span > 0 && hi < qw0 - r.span + 1);
 
@@ -241,7 +252,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       }
     }
 
-    if (idx + 1 < ntiles) store_tile(buf ^ 1);
+    if (idx + 1 < ntiles) store_tile(sK[buf ^ 1], sV[buf ^ 1], ld_row, ld_chunk, stK, stV);
     __syncthreads();
   }
 

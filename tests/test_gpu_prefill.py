@@ -31,7 +31,7 @@ def _gen(seed, B, N, hq, hkv):
 def _layer_kw(layer):
     return dict(hkv=layer.num_kv_heads, layer="sliding" if layer.kind == 1 else "full",
                 window=layer.window, sink=layer.sink, recent=layer.recent,
-                full_attention_heads=layer.full_attention_heads)
+                full_attention_heads=layer.full_attention_heads, scale=layer.scale)
 
 
 def run_chunked(lib, layer, q, k, v, chunk, want_lse=True):
