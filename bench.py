@@ -106,7 +106,7 @@ def bench_decode_sliding(torch, G, wl, timer, warmup, steps, replicas=8):
     out = torch.empty_like(q)
     sl = torch.tensor(L, dtype=torch.int32, device="cuda")
     maxlen = int(L.max())
-    ws = torch.empty(G.decode_workspace_bytes(layer, w.batch, maxlen) // 4 + 64, dtype=torch.float32, device="cuda")
+    ws = G.decode_workspace(layer, w.batch, maxlen)
     nbytes = int(sum(min(int(x), w.window) for x in L)) * w.hkv * 128 * 2 * 2
     log("decode sliding: timing")
     ms = timer.run(lambda i: G.attn_decode(layer, caches[i % replicas], q, sl, maxlen, out, ws), warmup, steps)
@@ -134,7 +134,7 @@ def bench_decode_duo(torch, G, wl, timer, warmup, steps, replicas=2):
     q = dev_bits(torch, wl.decode_queries(w.seed, w.batch, w.hq, 128))
     out = torch.empty_like(q)
     sl = torch.tensor(L, dtype=torch.int32, device="cuda")
-    ws = torch.empty(G.decode_workspace_bytes(layer, w.batch, w.len_hi) // 4 + 64, dtype=torch.float32, device="cuda")
+    ws = G.decode_workspace(layer, w.batch, w.len_hi)
     nf = sum(1 for m in mask if m)
     ns = w.hkv - nf
     sr = w.sink + w.recent

@@ -64,6 +64,7 @@ def load(path: str = LIB_PATH):
         "duo_attn_prefill": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, i64, P, P, P]),
         "duo_attn_decode": (ctypes.c_int, [LP, CP, i32, P, P, i64, P, P, P, sz, P]),
         "duo_attn_decode_workspace_bytes": (sz, [LP, i32, i64]),
+        "duo_attn_decode_workspace_init": (ctypes.c_int, [P, sz, P]),
         "duo_kv_cache_bytes": (ctypes.c_int, [LP, i32, i64, I64P, I64P]),
         "duo_head_plan": (ctypes.c_int, [LP, I32P, I32P, I32P, I32P]),
         "duo_prefill_plan": (ctypes.c_int, [LP, i32, i32, i64, I32P, I64P]),
@@ -186,6 +187,21 @@ def attn_prefill(layer: Layer, q, k, v, out, start_pos: int = 0, past: Optional[
 def decode_workspace_bytes(layer: Layer, batch: int, max_seq_len: int) -> int:
     cl = layer._c()
     return int(load().duo_attn_decode_workspace_bytes(ctypes.byref(cl), batch, int(max_seq_len)))
+
+
+def decode_workspace(layer: Layer, batch: int, max_seq_len: int, device="cuda"):
+    """A zero-filled decode workspace (float32 tensor, 256-byte aligned by the
+    caching allocator)."""
+    import torch
+    n = (decode_workspace_bytes(layer, batch, max_seq_len) + 3) // 4
+    ws = torch.empty(max(n, 64), dtype=torch.float32, device=device)
+    init_decode_workspace(ws)
+    return ws
+
+
+def init_decode_workspace(ws, stream=None):
+    nbytes = ws.numel() * ws.element_size()
+    _check(load().duo_attn_decode_workspace_init(_ptr(ws), nbytes, _stream(stream)))
 
 
 def attn_decode(layer: Layer, cache: KVCache, q, seq_lens, max_seq_len: int, out, workspace,

@@ -141,9 +141,10 @@ int build_prefill(const Layer& L, int32_t batch, int32_t T, int64_t start_pos, P
   return DUO_OK;
 }
 
-// ---- decode plan: keys per split chosen so the launch has about
-// kDecodeTargetItems work items (8192 waves would be 32 per CU), never
-// fewer than kDecodeMinSplit keys per split.
+// ---- decode plan: keys per workgroup split chosen so the launch has about
+// kDecodeTargetItems workgroups, a multiple of one tile per wave, never fewer
+// than kDecodeMinSplit keys and never more than kDecodeMaxSplits splits of one
+// sequence.
 int build_decode(const Layer& L, int32_t batch, int64_t max_seq_len, int64_t main_cap, DecodeParams* p) {
   std::memset(p, 0, sizeof(*p));
   p->batch = batch;
@@ -162,10 +163,14 @@ int build_decode(const Layer& L, int32_t batch, int64_t max_seq_len, int64_t mai
   const int64_t sr = (int64_t)L.sink + L.recent;
   const int64_t keys_stream = max_seq_len < sr ? max_seq_len : sr;
   const int64_t total = (int64_t)batch * (L.plan.n_main * keys_main + L.plan.n_stream * keys_stream);
+  const int64_t unit = (int64_t)kDecodeKeys * kDecodeWaves;
   int64_t split = (total + kDecodeTargetItems - 1) / kDecodeTargetItems;
-  split = (split + kDecodeKeys - 1) / kDecodeKeys * kDecodeKeys;
   if (split < kDecodeMinSplit) split = kDecodeMinSplit;
-  if (split > kMaxPos) split = kMaxPos / kDecodeKeys * kDecodeKeys;
+  const int64_t longest = keys_main > keys_stream ? keys_main : keys_stream;
+  const int64_t min_for_cap = (longest + kDecodeMaxSplits - 1) / kDecodeMaxSplits;
+  if (split < min_for_cap) split = min_for_cap;
+  split = (split + unit - 1) / unit * unit;
+  if (split > kMaxPos) split = kMaxPos / unit * unit;
   p->split_keys = (int32_t)split;
   p->n_split_main = L.plan.n_main > 0 ? (int32_t)((keys_main + split - 1) / split) : 0;
   p->n_split_stream = L.plan.n_stream > 0 ? (int32_t)((keys_stream + split - 1) / split) : 0;
@@ -180,12 +185,22 @@ int build_decode(const Layer& L, int32_t batch, int64_t max_seq_len, int64_t mai
   return DUO_OK;
 }
 
-size_t decode_ws_bytes(const DecodeParams& p) {
+// Workspace: [B * Hkv] int32 arrival counters | [B, Hq, splits, 2] partial
+// (max, sum) | [B, Hq, splits, 128] partial outputs; each part 256-byte aligned.
+struct WsLayout { size_t count, ml, acc, total; };
+
+WsLayout decode_ws_layout(const DecodeParams& p) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   const size_t n = (size_t)p.batch * p.hq * (size_t)p.n_split_max;
-  const size_t acc = n * kD * sizeof(float);
-  const size_t acc_padded = (acc + 255) / 256 * 256;
-  return acc_padded + n * 2 * sizeof(float);
+  WsLayout w;
+  w.count = 0;
+  w.ml = up((size_t)p.batch * p.hkv * sizeof(int32_t));
+  w.acc = w.ml + up(n * 2 * sizeof(float));
+  w.total = w.acc + n * kD * sizeof(float);
+  return w;
 }
+
+size_t decode_ws_bytes(const DecodeParams& p) { return decode_ws_layout(p).total; }
 
 }  // namespace
 
@@ -392,11 +407,20 @@ int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t b
   p.v_main = static_cast<const uint16_t*>(cache->v_main);
   p.k_stream = static_cast<const uint16_t*>(cache->k_stream);
   p.v_stream = static_cast<const uint16_t*>(cache->v_stream);
-  const size_t n = (size_t)p.batch * p.hq * (size_t)p.n_split_max;
-  const size_t acc = (n * kD * sizeof(float) + 255) / 256 * 256;
-  p.ws_acc = static_cast<float*>(workspace);
-  p.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + acc);
+  const WsLayout wl = decode_ws_layout(p);
+  char* ws = static_cast<char*>(workspace);
+  p.ws_count = reinterpret_cast<int32_t*>(ws + wl.count);
+  p.ws_ml = reinterpret_cast<float*>(ws + wl.ml);
+  p.ws_acc = reinterpret_cast<float*>(ws + wl.acc);
   return hip_status(launch_decode(p, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+int duo_attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (workspace == nullptr) return fail(DUO_ERR_INVALID_ARG, "workspace is NULL");
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DUO_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  return hip_status(launch_fill_zero(static_cast<int32_t*>(workspace), (int64_t)(workspace_bytes / 4),
+                                     static_cast<hipStream_t>(stream)),
+                    "workspace init launch");
 }
 
 }  // extern "C"

@@ -1,5 +1,5 @@
-// Decode attention kernels (gfx950): split-K partials that stream the KV cache
-// from HBM, and a merge of the partial softmax states.
+// Decode attention kernel (gfx950): split-K over the KV cache with the merge
+// of partial softmax states done in the same launch.
 //
 // One query token per sequence at position L-1 (its K/V already appended).
 // Full-context heads read every cached position, streaming heads read their
@@ -10,19 +10,23 @@
 // decode query, so a decode reads slots [0, n) in storage order; softmax does
 // not depend on key order.
 //
-// Partial kernel: one wave per (sequence, KV head, split). The G query heads
-// of the KV head are the 16 MFMA columns (G <= 16), so one pass over K/V
-// serves the whole group. 32-key tiles are loaded with 16-byte coalesced
-// loads, one tile ahead in registers, and go through a wave-private LDS tile
-// for the MFMA operand layouts (K row-major, V read transposed).
-// Merge kernel: one wave per (sequence, query head) combines the splits with
-// the usual max / rescale / sum over partial (m, l, acc).
+// Workgroup = 4 waves = one (sequence, KV head, split). The G query heads of
+// the KV head are the 16 MFMA columns (G <= 16): one pass over K/V serves the
+// whole group. Each wave streams its own interleaved 32-key tiles (16-byte
+// coalesced loads, one tile ahead in registers, a wave-private LDS tile for the
+// MFMA operand layouts: K row-major, V read transposed) and keeps its own
+// running (max, sum, output); the waves are combined through LDS.
+// A sequence whose keys fit one split is finished by its workgroup. Otherwise
+// each split stores its combined partial in the workspace and bumps the
+// group's arrival counter; the last workgroup to arrive merges all partials
+// (max, rescale, sum) and resets the counter to zero for the next call.
 #include "duo_internal.h"
 #include "mfma_common.h"
 
 namespace duo {
 
 constexpr int kDPitch = kD + 8;
+constexpr int kTileElems = kDecodeKeys * kDPitch;  // one K or V tile in LDS
 
 // One 32-key tile, global -> registers: rows ld_row + 4 j (clamped to the
 // split's last slot), 16-byte chunk ld_chunk; each load instruction of the
@@ -33,27 +37,138 @@ __device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t*
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     int64_t slot = k0 + ld_row + 4 * j;
-    slot = slot < k_end ? slot : k_end - 1;
+    slot = slot < k_end ? slot : k_end - 1;  // k_end >= 1 for a non-empty split
     stK[j] = *reinterpret_cast<const u32x4*>(kbase + slot * kD + ld_chunk * 8);
     stV[j] = *reinterpret_cast<const u32x4*>(vbase + slot * kD + ld_chunk * 8);
   }
 }
 
-__global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kDecodeKeys * kDPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kDecodeKeys * kDPitch];
+// Registers -> this wave's private LDS tile; the wave barrier orders the
+// previous tile's reads before the overwrite and these writes before the reads.
+__device__ __forceinline__ void stage_tile(uint16_t* sK, uint16_t* sV, int ld_row, int ld_chunk,
+                                           const u32x4 (&stK)[8], const u32x4 (&stV)[8]) {
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int off = (ld_row + 4 * j) * kDPitch + ld_chunk * 8;
+    *reinterpret_cast<u32x4*>(&sK[off]) = stK[j];
+    *reinterpret_cast<u32x4*>(&sV[off]) = stV[j];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// One 32-key tile from LDS: S^T = K Q^T, mask slots >= k_end, online softmax
+// update of (m, l, o) for the wave's 16 columns, O^T += V^T P^T.
+__device__ __forceinline__ void attend_tile(const uint16_t* sK, const uint16_t* sV, const bf16x8 (&qf)[4],
+                                            int64_t k0, int64_t k_end, float c, int r16, int g, float& m,
+                                            float& l, f32x4 (&o)[8]) {
+  f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[(16 * kt + r16) * kDPitch + 32 * ds + 8 * g]);
+      s[kt] = mfma_16x16x32(a, qf[ds], s[kt]);
+    }
+  }
+  if (k0 + kDecodeKeys > k_end) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (k0 + 16 * kt + 4 * g + i >= k_end) s[kt][i] = kNegInf;
+  }
+  float mx = s[0][0];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][i]);
+  mx = wave_xor_max(mx, 16);
+  mx = wave_xor_max(mx, 32);
+  mx *= c;
+  const bool up = mx > m + kRescaleThreshold;
+  if (__any(up)) {
+    const float a = up ? fast_exp2(m - mx) : 1.f;
+    m = up ? mx : m;
+    l *= a;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[dt] *= a;
+  }
+  const float mu = (m == kNegInf) ? 0.f : m;
+  float sum = 0.f;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = fast_exp2(__builtin_fmaf(s[kt][i], c, -mu));
+      s[kt][i] = e;
+      sum += e;
+    }
+  l += sum;
+  const bf16x8 pb = pack_bf16(s[0], s[1]);
+  const uint16_t* v0 = &sV[(4 * g + (r16 >> 2)) * kDPitch + 4 * (r16 & 3)];
+  const uint16_t* v1 = v0 + 16 * kDPitch;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const bf16x8 a = cat_bf16(lds_read_tr16(v0 + 16 * dt), lds_read_tr16(v1 + 16 * dt));
+    o[dt] = mfma_16x16x32(a, pb, o[dt]);
+  }
+}
+
+// Device-coherent (sc1) store / load: visible across XCDs without flushing
+// the L2 caches.
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void write_out_pair(const DecodeParams& p, int64_t bh, int dim, float a0, float a1,
+                                               float inv) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 r = __builtin_convertvector((f32x2{a0 * inv, a1 * inv}), bf16x2);
+  *reinterpret_cast<bf16x2*>(p.out + bh * kD + dim) = r;
+}
+
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
+  // K/V tiles of the 4 waves; reused after the key loop for the combine/merge.
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kDecodeWaves * 2 * kTileElems];
+  __shared__ float s_ml[kDecodeWaves][16][2];
+  __shared__ int s_last;
 
   const DecodeItem it = decode_item(p, blockIdx.x);
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int r16 = lane & 15;
   const int g = lane >> 4;
+  const int G = p.group;
 
   const int64_t len = p.seq_lens[it.b];
   const int64_t n_valid = decode_valid_slots(p, it.cls, len > 0 ? len : 0);
+  const int n_planned = (it.cls == kStream) ? p.n_split_stream : p.n_split_main;
+  int n_used = (int)((n_valid + p.split_keys - 1) / p.split_keys);
+  if (n_used > n_planned) n_used = n_planned;  // a length beyond the planned maximum is cut
   const int64_t k_begin = (int64_t)it.split * p.split_keys;
   int64_t k_end = k_begin + p.split_keys;
   if (k_end > n_valid) k_end = n_valid;
-  if (k_begin >= k_end) return;  // empty split: the merge does not read it
+  const int64_t bh0 = (int64_t)it.b * p.hq + (int64_t)it.kvh * G;  // first query head row
+
+  if (it.split >= n_used) {
+    // empty split; split 0 of an empty sequence writes the zero rows
+    if (it.split == 0) {
+      for (int e = tid; e < G * (kD / 2); e += 256) {
+        const int h = e / (kD / 2);
+        *reinterpret_cast<uint32_t*>(p.out + (bh0 + h) * kD + 2 * (e % (kD / 2))) = 0u;
+        if (p.lse != nullptr && (e % (kD / 2)) == 0) p.lse[bh0 + h] = kNegInf;
+      }
+    }
+    return;
+  }
 
   const uint16_t* kbase;
   const uint16_t* vbase;
@@ -70,8 +185,8 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
   // Q fragments: column r16 = query head kvh * G + r16 (zero beyond G).
   bf16x8 qf[4];
   {
-    const bool ok = r16 < p.group;
-    const uint16_t* src = p.q + ((int64_t)it.b * p.hq + it.kvh * p.group + (ok ? r16 : 0)) * kD + 8 * g;
+    const bool ok = r16 < G;
+    const uint16_t* src = p.q + (bh0 + (ok ? r16 : 0)) * kD + 8 * g;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
       u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(src + 32 * ds) : u32x4{0u, 0u, 0u, 0u};
@@ -79,10 +194,10 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
     }
   }
 
-  // staging: rows (lane / 16) + 4 j, chunk lane % 16
+  uint16_t* sK = smem + wave * 2 * kTileElems;
+  uint16_t* sV = sK + kTileElems;
   const int ld_row = lane >> 4;
   const int ld_chunk = lane & 15;
-  u32x4 stK[8], stV[8];
 
   const float c = p.scale_log2;
   float m = kNegInf, l = 0.f;
@@ -90,134 +205,193 @@ __global__ __launch_bounds__(64) void decode_partial_kernel(DecodeParams p) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_tile(kbase, vbase, k_begin, k_end, ld_row, ld_chunk, stK, stV);
-  for (int64_t k0 = k_begin; k0 < k_end; k0 += kDecodeKeys) {
-    __syncthreads();  // previous tile's LDS reads are done
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int off = (ld_row + 4 * j) * kDPitch + ld_chunk * 8;
-      *reinterpret_cast<u32x4*>(&sK[off]) = stK[j];
-      *reinterpret_cast<u32x4*>(&sV[off]) = stV[j];
-    }
-    __syncthreads();
-    if (k0 + kDecodeKeys < k_end) load_tile(kbase, vbase, k0 + kDecodeKeys, k_end, ld_row, ld_chunk, stK, stV);
-
-    f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[(16 * kt + r16) * kDPitch + 32 * ds + 8 * g]);
-        s[kt] = mfma_16x16x32(a, qf[ds], s[kt]);
-      }
-    }
-    if (k0 + kDecodeKeys > k_end) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (k0 + 16 * kt + 4 * g + i >= k_end) s[kt][i] = kNegInf;
-    }
-    float mx = s[0][0];
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][i]);
-    mx = wave_xor_max(mx, 16);
-    mx = wave_xor_max(mx, 32);
-    mx *= c;
-    const bool up = mx > m + kRescaleThreshold;
-    if (__any(up)) {
-      const float a = up ? fast_exp2(m - mx) : 1.f;
-      m = up ? mx : m;
-      l *= a;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[dt] *= a;
-    }
-    const float mu = (m == kNegInf) ? 0.f : m;
-    float sum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = fast_exp2(__builtin_fmaf(s[kt][i], c, -mu));
-        s[kt][i] = e;
-        sum += e;
-      }
-    l += sum;
-    const bf16x8 pb = pack_bf16(s[0], s[1]);
-    const uint16_t* v0 = &sV[(4 * g + (r16 >> 2)) * kDPitch + 4 * (r16 & 3)];
-    const uint16_t* v1 = v0 + 16 * kDPitch;
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const bf16x8 a = cat_bf16(lds_read_tr16(v0 + 16 * dt), lds_read_tr16(v1 + 16 * dt));
-      o[dt] = mfma_16x16x32(a, pb, o[dt]);
-    }
+  // This wave's tiles start at k_begin + 32 * (wave + 4 t). Two tiles are kept
+  // in flight (register buffers A and B, used alternately). Loads are issued
+  // unconditionally so the wait counts stay exact: a tile past the split end
+  // reads the last valid slot and is fully masked, leaving (m, l, o) unchanged.
+  const int64_t stride = (int64_t)kDecodeKeys * kDecodeWaves;
+  const int64_t first = k_begin + (int64_t)kDecodeKeys * wave;
+  const int64_t nt = first < k_end ? (k_end - first + stride - 1) / stride : 0;
+  u32x4 aK[8], aV[8], bK[8], bV[8];
+  // (scheduling barriers keep each tile's 16 loads contiguous in issue order,
+  // so waiting for one buffer never waits for the other)
+  load_tile(kbase, vbase, first, k_end, ld_row, ld_chunk, aK, aV);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(kbase, vbase, first + stride, k_end, ld_row, ld_chunk, bK, bV);
+  __builtin_amdgcn_sched_barrier(0);
+  for (int64_t t = 0; t < nt; t += 2) {
+    const int64_t k0 = first + t * stride;
+    stage_tile(sK, sV, ld_row, ld_chunk, aK, aV);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(kbase, vbase, k0 + 2 * stride, k_end, ld_row, ld_chunk, aK, aV);
+    __builtin_amdgcn_sched_barrier(0);
+    attend_tile(sK, sV, qf, k0, k_end, c, r16, g, m, l, o);
+    __builtin_amdgcn_sched_barrier(0);
+    stage_tile(sK, sV, ld_row, ld_chunk, bK, bV);
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(kbase, vbase, k0 + 3 * stride, k_end, ld_row, ld_chunk, bK, bV);
+    __builtin_amdgcn_sched_barrier(0);
+    attend_tile(sK, sV, qf, k0 + stride, k_end, c, r16, g, m, l, o);
+    __builtin_amdgcn_sched_barrier(0);
   }
-
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (r16 >= p.group) return;
-  const int h = it.kvh * p.group + r16;
-  const int64_t slot = ((int64_t)it.b * p.hq + h) * p.n_split_max + it.split;
-  float* acc = p.ws_acc + slot * kD + 4 * g;
+
+  // ---- combine the 4 waves: acc[w][col][dim] in LDS (reuses the tile area)
+  __syncthreads();
+  float* comb = reinterpret_cast<float*>(smem);  // [4][16][128] floats = 32 KB
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4*>(acc + 16 * dt) = o[dt];
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<f32x4*>(&comb[(wave * 16 + r16) * kD + 16 * dt + 4 * g]) = o[dt];
   if (g == 0) {
-    p.ws_ml[slot * 2 + 0] = m;
-    p.ws_ml[slot * 2 + 1] = l;
+    s_ml[wave][r16][0] = m;
+    s_ml[wave][r16][1] = l;
   }
+  __syncthreads();
+
+  // thread -> (column, dim pair) of the G valid columns; 64 threads per column
+  const bool single = (n_used == 1);
+  for (int e = tid; e < G * (kD / 2); e += 256) {
+    const int col = e / (kD / 2);
+    const int dim = 2 * (e % (kD / 2));
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, s_ml[w][col][0]);
+    float L = 0.f, a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float mw = s_ml[w][col][0];
+      const float sc = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
+      L += sc * s_ml[w][col][1];
+      a0 += sc * comb[(w * 16 + col) * kD + dim];
+      a1 += sc * comb[(w * 16 + col) * kD + dim + 1];
+    }
+    const int64_t bh = bh0 + col;
+    if (single) {
+      write_out_pair(p, bh, dim, a0, a1, 1.f / L);
+      if (p.lse != nullptr && dim == 0) p.lse[bh] = (M + __log2f(L)) * kLn2;
+    } else {
+      const int64_t slot = bh * p.n_split_max + it.split;
+      coherent_store(p.ws_acc + slot * kD + dim, a0);
+      coherent_store(p.ws_acc + slot * kD + dim + 1, a1);
+      if (dim == 0) {
+        coherent_store(p.ws_ml + slot * 2 + 0, M);
+        coherent_store(p.ws_ml + slot * 2 + 1, L);
+      }
+    }
+  }
+  if (single) return;
+
+  // ---- split-K: publish this partial; the last workgroup of the group merges.
+  // Partials travel through device-coherent (sc1) stores and loads, which
+  // bypass the per-XCD L2 caches; each wave drains its stores before the
+  // arrival counter is bumped, so no cache-wide writeback fence is needed.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  int32_t* counter = p.ws_count + (int64_t)it.b * p.hkv + it.kvh;
+  if (tid == 0)
+    s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_used - 1);
+  __syncthreads();
+  if (!s_last) return;
+
+  // (max, sum) of every (column, split) into LDS with all loads in flight,
+  // then per-column max / weights / normaliser, then the weighted sum of the
+  // partial outputs (wave w takes splits w, w+4, ...; 4 splits per batch).
+  float* s_m = reinterpret_cast<float*>(smem);  // [16][kDecodeMaxSplits]
+  float* s_w = s_m + 16 * kDecodeMaxSplits;       // [16][kDecodeMaxSplits] weights
+  float* s_L = s_w + 16 * kDecodeMaxSplits;       // [16]
+  float* red = s_L + 16;                          // [4][16][128]
+  for (int e = tid; e < G * n_used; e += 256) {
+    const int h = e / n_used, sp = e % n_used;
+    const float* ml = p.ws_ml + ((bh0 + h) * p.n_split_max + sp) * 2;
+    s_m[h * kDecodeMaxSplits + sp] = coherent_load(ml);
+    s_w[h * kDecodeMaxSplits + sp] = coherent_load(ml + 1);
+  }
+  __syncthreads();
+  for (int h = wave; h < G; h += kDecodeWaves) {
+    float M = kNegInf;
+    for (int sp = lane; sp < n_used; sp += 64) M = fmaxf(M, s_m[h * kDecodeMaxSplits + sp]);
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+    float L = 0.f;
+    for (int sp = lane; sp < n_used; sp += 64) {
+      const float w = fast_exp2(s_m[h * kDecodeMaxSplits + sp] - M);
+      L += w * s_w[h * kDecodeMaxSplits + sp];
+      s_w[h * kDecodeMaxSplits + sp] = w;
+    }
+#pragma unroll
+    for (int x = 32; x >= 1; x >>= 1) L += __shfl_xor(L, x);
+    if (lane == 0) {
+      s_L[h] = L;
+      if (p.lse != nullptr) p.lse[bh0 + h] = (M + __log2f(L)) * kLn2;
+    }
+  }
+  __syncthreads();
+  float acc[kMaxGroup][2];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) acc[h][0] = acc[h][1] = 0.f;
+  constexpr int kBatch = 4;
+  for (int sp0 = wave; sp0 < n_used; sp0 += kDecodeWaves * kBatch) {
+    float v[kBatch][kMaxGroup][2];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int sp = sp0 + u * kDecodeWaves;
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h) {
+        if (h < G && sp < n_used) {
+          const float* src = p.ws_acc + ((bh0 + h) * p.n_split_max + sp) * kD + 2 * lane;
+          v[u][h][0] = coherent_load(src);
+          v[u][h][1] = coherent_load(src + 1);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int sp = sp0 + u * kDecodeWaves;
+#pragma unroll
+      for (int h = 0; h < kMaxGroup; ++h) {
+        if (h < G && sp < n_used) {
+          const float w = s_w[h * kDecodeMaxSplits + sp];
+          acc[h][0] += w * v[u][h][0];
+          acc[h][1] += w * v[u][h][1];
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    if (h < G) {
+      red[(wave * 16 + h) * kD + 2 * lane] = acc[h][0];
+      red[(wave * 16 + h) * kD + 2 * lane + 1] = acc[h][1];
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < G * (kD / 2); e += 256) {
+    const int col = e / (kD / 2);
+    const int dim = 2 * (e % (kD / 2));
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      a0 += red[(w * 16 + col) * kD + dim];
+      a1 += red[(w * 16 + col) * kD + dim + 1];
+    }
+    write_out_pair(p, bh0 + col, dim, a0, a1, 1.f / s_L[col]);
+  }
+  if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
 }
 
-__global__ __launch_bounds__(256) void decode_merge_kernel(DecodeParams p) {
-  const int lane = threadIdx.x & 63;
-  const int64_t bh = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (bh >= (int64_t)p.batch * p.hq) return;
-  const int b = (int)(bh / p.hq);
-  const int h = (int)(bh % p.hq);
-  const int kvh = h / p.group;
-  const int cls = ((p.stream_mask >> kvh) & 1u) ? kStream : kMain;
-  const int64_t len = p.seq_lens[b];
-  const int64_t n_valid = decode_valid_slots(p, cls, len > 0 ? len : 0);
-  int n_used = (int)((n_valid + p.split_keys - 1) / p.split_keys);
-  // a length beyond the max_seq_len the grid was planned for is cut to the
-  // planned splits (never read past the workspace)
-  const int n_planned = (cls == kStream) ? p.n_split_stream : p.n_split_main;
-  if (n_used > n_planned) n_used = n_planned;
-  uint16_t* dst = p.out + bh * kD + 2 * lane;
-  if (n_used == 0) {
-    *reinterpret_cast<uint32_t*>(dst) = 0u;
-    if (p.lse != nullptr && lane == 0) p.lse[bh] = kNegInf;
-    return;
-  }
-  const float* ml = p.ws_ml + bh * p.n_split_max * 2;
-  float M = kNegInf;
-  for (int s = 0; s < n_used; ++s) M = fmaxf(M, ml[2 * s]);
-  float L = 0.f, a0 = 0.f, a1 = 0.f;
-  const float* acc = p.ws_acc + bh * p.n_split_max * kD + 2 * lane;
-  for (int s = 0; s < n_used; ++s) {
-    const float w = fast_exp2(ml[2 * s] - M);
-    L += w * ml[2 * s + 1];
-    const float2 v = *reinterpret_cast<const float2*>(acc + (int64_t)s * kD);
-    a0 += w * v.x;
-    a1 += w * v.y;
-  }
-  const float inv = 1.f / L;
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 r = __builtin_convertvector((f32x2{a0 * inv, a1 * inv}), bf16x2);
-  *reinterpret_cast<bf16x2*>(dst) = r;
-  if (p.lse != nullptr && lane == 0) p.lse[bh] = (M + __log2f(L)) * kLn2;
+__global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
-  if (p.n_items > 0) {
-    hipLaunchKernelGGL(decode_partial_kernel, dim3((unsigned)p.n_items), dim3(64), 0, s, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  const int64_t waves = (int64_t)p.batch * p.hq;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, s, p);
+  if (p.n_items > 0) hipLaunchKernelGGL(decode_kernel, dim3((unsigned)p.n_items), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n);
   return hipGetLastError();
 }
 

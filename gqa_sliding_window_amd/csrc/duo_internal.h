@@ -11,12 +11,22 @@ namespace duo {
 
 constexpr int kD = 128;           // head_dim
 constexpr int kMaxKv = 32;        // KV heads per layer
+constexpr int kMaxGroup = 16;     // query heads per KV head (MFMA columns)
 constexpr int kPrefillRows = 128; // query rows per prefill workgroup (4 waves x 32)
 constexpr int kPrefillKeys = 64;  // keys per prefill K/V tile
 constexpr int kDecodeKeys = 32;   // keys per decode tile (one wave)
+constexpr int kDecodeWaves = 4;   // waves per decode workgroup
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
-constexpr int kDecodeTargetItems = 4096;
-constexpr int kDecodeMinSplit = 128;
+// Decode split planning (overridable at build time for tuning sweeps).
+#ifndef DUO_DECODE_TARGET_ITEMS
+#define DUO_DECODE_TARGET_ITEMS 640       // ~2.5 workgroups per CU
+#endif
+#ifndef DUO_DECODE_MIN_SPLIT
+#define DUO_DECODE_MIN_SPLIT 512          // keys per workgroup, at least 4 tiles per wave
+#endif
+constexpr int kDecodeTargetItems = DUO_DECODE_TARGET_ITEMS;
+constexpr int kDecodeMinSplit = DUO_DECODE_MIN_SPLIT;
+constexpr int kDecodeMaxSplits = 256;     // splits of one sequence (bounds the merge)
 
 enum HeadClass : int { kMain = 0, kStream = 1 };
 
@@ -178,8 +188,9 @@ struct DecodeParams {
   const uint16_t* v_main;
   const uint16_t* k_stream;
   const uint16_t* v_stream;
-  float* ws_acc;         // [B, Hq, n_split_max, D]
-  float* ws_ml;          // [B, Hq, n_split_max, 2]
+  int32_t* ws_count;     // [B, Hkv] arrival counters, zero between calls
+  float* ws_ml;          // [B, Hq, n_split_max, 2] partial (max, sum)
+  float* ws_acc;         // [B, Hq, n_split_max, D] partial unnormalised outputs
   int64_t main_cap;      // slots per (b, main head)
   int32_t main_ring;     // main cache is a ring (sliding layer)
   int32_t batch, hq, hkv, group;
@@ -224,5 +235,6 @@ __host__ __device__ inline int64_t decode_valid_slots(const DecodeParams& p, int
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int64_t n_blocks, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s);
 
 }  // namespace duo

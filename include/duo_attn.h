@@ -146,12 +146,21 @@ int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t b
  * max_seq_len : host bound used to size the split-K grid.
  * out       : device [batch, Hq, 128] bf16.  lse: NULL or device float [batch, Hq].
  * workspace : device scratch of at least duo_attn_decode_workspace_bytes()
- *             bytes, 256-byte aligned, owned by the caller; holds split-K
- *             partial results between the two kernels of one call. */
+ *             bytes, 256-byte aligned, owned by the caller. It holds split-K
+ *             partial results and per-(sequence, KV head) arrival counters.
+ *             It must be zero-filled once before its first use
+ *             (duo_attn_decode_workspace_init, or any zero fill); every
+ *             completed call leaves the counters at zero again, so it can be
+ *             reused without clearing. Calls that share a workspace must be
+ *             ordered (same stream). */
 int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch,
                     const void* q, const int32_t* seq_lens, int64_t max_seq_len,
                     void* out, float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* Zero-fill a decode workspace (enqueued on `stream`; a small fill kernel, so
+ * it is also safe under graph capture). */
+int duo_attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace size for duo_attn_decode; 0 on invalid arguments. Host only. */
 size_t duo_attn_decode_workspace_bytes(const duo_layer* layer, int32_t batch,

@@ -42,10 +42,10 @@ def fill_cache(lib, layer, cache, seqs, chunk=1 << 20):
     torch.cuda.synchronize()
 
 
-def run_decode(lib, layer, cache, q, lengths, max_len):
+def run_decode(lib, layer, cache, q, lengths, max_len, ws=None):
     import torch
     B, hq, _ = q.shape
-    ws = torch.empty(lib.decode_workspace_bytes(layer, B, max_len) // 4 + 64, dtype=torch.float32, device="cuda")
+    ws = lib.decode_workspace(layer, B, max_len) if ws is None else ws
     out = torch.empty((B, hq, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
     sl = torch.tensor(lengths, dtype=torch.int32, device="cuda")
@@ -102,8 +102,13 @@ def test_duo_decode_workload(lib):
     cache = lib.KVCache(layer, w.batch, w.len_hi, zero=False)
     fill_cache(lib, layer, cache, seqs, chunk=32768)
     q = wl.decode_queries(w.seed, w.batch, w.hq, 128)
-    out, lse = run_decode(lib, layer, cache, q, L, w.len_hi)
+    ws = lib.decode_workspace(layer, w.batch, w.len_hi)
+    out, lse = run_decode(lib, layer, cache, q, L, w.len_hi, ws)
     check_decode(layer, q, seqs, out, lse, w.name)
+    # split-K arrival counters are back at zero: a second call on the same
+    # workspace gives the same bits
+    out2, lse2 = run_decode(lib, layer, cache, q, L, w.len_hi, ws)
+    np.testing.assert_array_equal(out2, out)
 
 
 SMALL = {
@@ -129,10 +134,13 @@ def test_decode_small(lib, name):
     q = wl.decode_queries(zlib.crc32(name.encode()) % 1000 + 1, len(L), layer.num_q_heads, 128)
     out, lse = run_decode(lib, layer, cache, q, L, max(L))
     check_decode(layer, q, seqs, out, lse, name)
-    # a larger max_seq_len hint changes the split plan, not the result
-    out2, lse2 = run_decode(lib, layer, cache, q, L, big)
-    d = np.abs(bits_to_f64(out2) - bits_to_f64(out)).max()
-    assert d <= 1.6e-2, d
+    # a larger max_seq_len hint changes the split plan, not the result; the
+    # second call on the same workspace checks the counters were reset
+    ws = lib.decode_workspace(layer, len(L), big)
+    for _ in range(2):
+        out2, lse2 = run_decode(lib, layer, cache, q, L, big, ws)
+        d = np.abs(bits_to_f64(out2) - bits_to_f64(out)).max()
+        assert d <= 1.6e-2, d
 
 
 def test_zero_length_rows(lib):
