@@ -16,66 +16,96 @@
 // outside the ranges are never visited and only tiles on a range edge, the
 // diagonal or a band edge evaluate the per-element predicate. Keys before
 // start_pos are read from the cache (slot per class), the chunk's own keys
-// from the k/v inputs.
+// from the k/v inputs. Positions are 32-bit (the host bounds them below 2^31);
+// a tile that lies wholly in the chunk or in a contiguous stretch of the cache
+// is addressed from one base pointer, other tiles row by row.
 #include "duo_internal.h"
 #include "mfma_common.h"
 
 namespace duo {
 
 constexpr int kPitch = kD + 8;  // LDS row pitch in bf16 elements (272 bytes)
+constexpr int kNegBig = -0x7fffffff;
 
-struct RowSrc {
+struct TileRange {
+  int lo, hi;      // visible key positions of the range (inclusive)
+  int span;        // > 0: causal band of this width ending at the query
+  int first;       // first tile start (lo rounded down to 64)
+};
+
+struct Src {
   const uint16_t* k;
   const uint16_t* v;
 };
 
-// Address of key position `pos` for (b, kvh): chunk input or cache slot.
-__device__ __forceinline__ RowSrc key_row(const PrefillParams& p, const PrefillItem& it,
-                                          int64_t pos) {
-  RowSrc r;
-  if (pos >= p.start_pos) {
-    const int64_t off = (((int64_t)it.b * p.T + (pos - p.start_pos)) * p.hkv + it.kvh) * kD;
-    r.k = p.k + off;
-    r.v = p.v + off;
-    return r;
-  }
-  int64_t off;
-  if (it.cls == kStream) {
-    const int64_t cap = (int64_t)p.sink + p.recent;
-    const int64_t slot = pos < p.sink ? pos : p.sink + (pos - p.sink) % p.recent;
-    off = (((int64_t)it.b * p.n_stream + it.rank) * cap + slot) * kD;
-    r.k = p.k_stream + off;
-    r.v = p.v_stream + off;
+// Everything the loader needs about one (sequence, KV head).
+struct KvSrc {
+  const uint16_t* ck;    // chunk K/V at position P, this (b, kvh)
+  const uint16_t* cv;
+  int64_t cstride;       // elements between consecutive chunk positions
+  const uint16_t* mk;    // cache rows of this (b, class, rank), slot 0
+  const uint16_t* mv;
+  int P;                 // start_pos
+  int cls;
+  int ring_cap;          // main ring capacity (0 = contiguous main cache)
+  int sink, recent;
+};
+
+// Cache slot of a past position (library slot contract, see duo_attn.h).
+__device__ __forceinline__ int cache_slot(const KvSrc& s, int pos) {
+  if (s.cls == kStream) return pos < s.sink ? pos : s.sink + (pos - s.sink) % s.recent;
+  return s.ring_cap ? pos % s.ring_cap : pos;
+}
+
+__device__ __forceinline__ Src row_src(const KvSrc& s, int pos) {
+  Src r;
+  if (pos >= s.P) {
+    const int64_t off = (int64_t)(pos - s.P) * s.cstride;
+    r.k = s.ck + off;
+    r.v = s.cv + off;
   } else {
-    const int64_t slot = p.main_ring ? pos % p.main_cap : pos;
-    off = (((int64_t)it.b * p.n_main + it.rank) * p.main_cap + slot) * kD;
-    r.k = p.k_main + off;
-    r.v = p.v_main + off;
+    const int64_t off = (int64_t)cache_slot(s, pos) * kD;
+    r.k = s.mk + off;
+    r.v = s.mv + off;
   }
   return r;
 }
 
-// Tile idx of the (at most two) key ranges: its range and first position.
-__device__ __forceinline__ void tile_of(const KeyRange (&rg)[2], int64_t nt0, int64_t idx, KeyRange& r,
-                                        int64_t& lo) {
-  const bool first = idx < nt0;
-  r = first ? rg[0] : rg[1];
-  lo = (r.lo / kPrefillKeys + (first ? idx : idx - nt0)) * kPrefillKeys;
-}
-
-// Global -> registers: rows ld_row + 16 j of the tile; positions outside the
-// range are clamped onto it (their logits are masked, their values finite).
-__device__ __forceinline__ void load_tile(const PrefillParams& p, const PrefillItem& it,
-                                          const KeyRange (&rg)[2], int64_t nt0, int64_t idx, int ld_row,
-                                          int ld_chunk, u32x4 (&stK)[4], u32x4 (&stV)[4]) {
-  KeyRange r;
-  int64_t lo;
-  tile_of(rg, nt0, idx, r, lo);
+// Global -> registers for the tile starting at `lo` of range r: rows
+// ld_row + 16 j. Positions outside the range are clamped onto it (their
+// logits are masked; their values are finite data).
+__device__ __forceinline__ void load_tile(const KvSrc& s, const TileRange& r, int lo, int ld_row, int ld_chunk,
+                                          u32x4 (&stK)[4], u32x4 (&stV)[4]) {
+  const int hi = lo + kPrefillKeys - 1;
+  const bool inside = lo >= r.lo && hi <= r.hi;
+  if (inside && lo >= s.P) {
+    // whole tile in the chunk: one base, constant row stride
+    const int64_t base = (int64_t)(lo - s.P) * s.cstride + ld_chunk * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t off = base + (int64_t)(ld_row + 16 * j) * s.cstride;
+      stK[j] = *reinterpret_cast<const u32x4*>(s.ck + off);
+      stV[j] = *reinterpret_cast<const u32x4*>(s.cv + off);
+    }
+    return;
+  }
+  const bool contiguous_cache = hi < s.P && (s.cls == kStream ? hi < s.sink : s.ring_cap == 0);
+  if (inside && contiguous_cache) {
+    // whole tile in a stretch of the cache where slot = position
+    const int64_t base = (int64_t)lo * kD + ld_chunk * 8;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t off = base + (int64_t)(ld_row + 16 * j) * kD;
+      stK[j] = *reinterpret_cast<const u32x4*>(s.mk + off);
+      stV[j] = *reinterpret_cast<const u32x4*>(s.mv + off);
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    int64_t pos = lo + ld_row + 16 * j;
+    int pos = lo + ld_row + 16 * j;
     pos = pos < r.lo ? r.lo : (pos > r.hi ? r.hi : pos);
-    const RowSrc src = key_row(p, it, pos);
+    const Src src = row_src(s, pos);
     stK[j] = *reinterpret_cast<const u32x4*>(src.k + ld_chunk * 8);
     stV[j] = *reinterpret_cast<const u32x4*>(src.v + ld_chunk * 8);
   }
@@ -104,21 +134,21 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
-  const int64_t P0 = p.start_pos;
-  const int64_t qa = P0 + (int64_t)it.qtile * kPrefillRows;
-  const int64_t last = P0 + p.T - 1;
-  const int64_t qb = (qa + kPrefillRows - 1 < last) ? qa + kPrefillRows - 1 : last;
-  const int64_t qw0 = qa + wave * 32;
-  const int64_t qw1 = (qw0 + 31 < qb) ? qw0 + 31 : qb;
+  const int P = (int)p.start_pos;
+  const int last = P + p.T - 1;
+  const int qa = P + it.qtile * kPrefillRows;
+  const int qb = min(qa + kPrefillRows - 1, last);
+  const int qw0 = qa + wave * 32;
+  const int qw1 = min(qw0 + 31, qb);
   const bool wave_active = qw0 <= qb;
 
   // ---- Q fragments (B operand of S^T = K Q^T): row qw0 + 16t + r16.
   bf16x8 qf[2][4];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int64_t qpos = qw0 + 16 * t + r16;
+    const int qpos = qw0 + 16 * t + r16;
     const bool ok = qpos <= qb;
-    const uint16_t* src = p.q + (((int64_t)it.b * p.T + (ok ? qpos - P0 : 0)) * p.hq + it.qhead) * kD + 8 * g;
+    const uint16_t* src = p.q + (((int64_t)it.b * p.T + (ok ? qpos - P : 0)) * p.hq + it.qhead) * kD + 8 * g;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
       u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(src + 32 * ds) : u32x4{0u, 0u, 0u, 0u};
@@ -126,10 +156,43 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     }
   }
 
-  KeyRange rg[2];
-  const int nr = prefill_key_ranges(p, it.cls, qa, qb, rg);
-  const int64_t nt0 = tiles_of(rg[0]);
-  const int64_t ntiles = nt0 + (nr > 1 ? tiles_of(rg[1]) : 0);
+  // ---- key ranges of this work item
+  TileRange rg0, rg1;
+  int nt0, ntiles;
+  {
+    KeyRange kr[2];
+    const int nr = prefill_key_ranges(p, it.cls, qa, qb, kr);
+    rg0 = TileRange{(int)kr[0].lo, (int)kr[0].hi, (int)kr[0].span, (int)(kr[0].lo / kPrefillKeys) * kPrefillKeys};
+    nt0 = (int)tiles_of(kr[0]);
+    ntiles = nt0;
+    rg1 = rg0;
+    if (nr > 1) {
+      rg1 = TileRange{(int)kr[1].lo, (int)kr[1].hi, (int)kr[1].span, (int)(kr[1].lo / kPrefillKeys) * kPrefillKeys};
+      ntiles += (int)tiles_of(kr[1]);
+    }
+  }
+
+  KvSrc src;
+  src.cstride = (int64_t)p.hkv * kD;
+  {
+    const int64_t coff = ((int64_t)it.b * p.T * p.hkv + it.kvh) * kD;
+    src.ck = p.k + coff;
+    src.cv = p.v + coff;
+  }
+  src.P = P;
+  src.cls = it.cls;
+  src.ring_cap = p.main_ring ? (int)p.main_cap : 0;
+  src.sink = p.sink;
+  src.recent = p.recent;
+  if (it.cls == kStream) {
+    const int64_t off = ((int64_t)it.b * p.n_stream + it.rank) * (int64_t)(p.sink + p.recent) * kD;
+    src.mk = p.k_stream + off;
+    src.mv = p.v_stream + off;
+  } else {
+    const int64_t off = ((int64_t)it.b * p.n_main + it.rank) * p.main_cap * kD;
+    src.mk = p.k_main + off;
+    src.mv = p.v_main + off;
+  }
 
   // ---- per-thread staging of one K/V tile: rows (tid/16) + 16 j, 16-byte chunk tid%16
   const int ld_row = tid >> 4;
@@ -146,23 +209,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_tile(p, it, rg, nt0, 0, ld_row, ld_chunk, stK, stV);
+  load_tile(src, rg0, rg0.first, ld_row, ld_chunk, stK, stV);
   store_tile(sK[0], sV[0], ld_row, ld_chunk, stK, stV);
   __syncthreads();
 
-  for (int64_t idx = 0; idx < ntiles; ++idx) {
-    const int buf = (int)(idx & 1);
-    if (idx + 1 < ntiles) load_tile(p, it, rg, nt0, idx + 1, ld_row, ld_chunk, stK, stV);
-
-    KeyRange r;
-    int64_t lo;
-    tile_of(rg, nt0, idx, r, lo);
-    const int64_t hi = lo + kPrefillKeys - 1;
+  for (int idx = 0; idx < ntiles; ++idx) {
+    const int buf = idx & 1;
+    if (idx + 1 < ntiles) {
+      const bool first_range = idx + 1 < nt0;
+      const TileRange rn = first_range ? rg0 : rg1;
+      const int lon = first_range ? rg0.first + kPrefillKeys * (idx + 1) : rg1.first + kPrefillKeys * (idx + 1 - nt0);
+      load_tile(src, rn, lon, ld_row, ld_chunk, stK, stV);
+    }
+    const bool first_range = idx < nt0;
+    const TileRange r = first_range ? rg0 : rg1;
+    const int lo = first_range ? rg0.first + kPrefillKeys * idx : rg1.first + kPrefillKeys * (idx - nt0);
+    const int hi = lo + kPrefillKeys - 1;
     const bool invisible = !wave_active || lo > qw1 || (r.span > 0 && hi < qw0 - r.span + 1);
 
     if (!invisible) {
-      const bool need_mask = !(lo >= r.lo && hi <= r.hi && hi <= qw0 &&
-                               (r.span == 0 || lo >= qw1 - r.span + 1));
+      const bool need_mask = !(lo >= r.lo && hi <= r.hi && hi <= qw0 && (r.span == 0 || lo >= qw1 - r.span + 1));
       // S^T = K Q^T for 64 keys x 32 rows
       f32x4 s[2][4];
 #pragma unroll
@@ -179,46 +245,46 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
         }
       }
       if (need_mask) {
+        // row q sees keys in [klo, khi]
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int64_t q = qw0 + 16 * t + r16;
+          const int q = qw0 + 16 * t + r16;
+          const int klo = max(r.lo, r.span > 0 ? q - r.span + 1 : kNegBig);
+          const int khi = min(r.hi, q);
+          const int base = lo + 4 * g;
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              const int64_t key = lo + 16 * kt + 4 * g + i;
-              const bool vis = key >= r.lo && key <= r.hi && key <= q &&
-                               (r.span == 0 || key > q - r.span);
-              if (!vis) s[t][kt][i] = kNegInf;
+              const int key = base + 16 * kt + i;
+              if (key < klo || key > khi) s[t][kt][i] = kNegInf;
             }
         }
       }
-      // online softmax, per row (lane column), stats shared by the 4 lanes of a row
-      float mx[2];
+      // Online softmax. Each lane holds 16 logits of each of its two rows; the
+      // 4 lanes of a row share the row maximum. The maximum only moves when
+      // some lane's logits exceed it by the rescale threshold, so the
+      // cross-lane exchange is skipped on most tiles.
+      float lmx[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        float v = s[t][0][0];
+        float v = fmaxf(fmaxf(s[t][0][0], s[t][0][1]), fmaxf(s[t][0][2], s[t][0][3]));
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v = fmaxf(v, s[t][kt][i]);
-        v = wave_xor_max(v, 16);
-        v = wave_xor_max(v, 32);
-        mx[t] = v * c;
+        for (int kt = 1; kt < 4; ++kt)
+          v = fmaxf(fmaxf(v, fmaxf(s[t][kt][0], s[t][kt][1])), fmaxf(s[t][kt][2], s[t][kt][3]));
+        lmx[t] = v * c;
       }
-      const bool up0 = mx[0] > m[0] + kRescaleThreshold;
-      const bool up1 = mx[1] > m[1] + kRescaleThreshold;
-      if (__any(up0 || up1)) {
-        const float a0 = up0 ? fast_exp2(m[0] - mx[0]) : 1.f;
-        const float a1 = up1 ? fast_exp2(m[1] - mx[1]) : 1.f;
-        m[0] = up0 ? mx[0] : m[0];
-        m[1] = up1 ? mx[1] : m[1];
-        l[0] *= a0;
-        l[1] *= a1;
+      if (__any(lmx[0] > m[0] + kRescaleThreshold || lmx[1] > m[1] + kRescaleThreshold)) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-          o[0][dt] *= a0;
-          o[1][dt] *= a1;
+        for (int t = 0; t < 2; ++t) {
+          float mx = wave_xor_max(lmx[t], 16);
+          mx = wave_xor_max(mx, 32);
+          const bool up = mx > m[t] + kRescaleThreshold;
+          const float a = up ? fast_exp2(m[t] - mx) : 1.f;
+          m[t] = up ? mx : m[t];
+          l[t] *= a;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) o[t][dt] *= a;
         }
       }
       bf16x8 pb[2][2];
@@ -263,10 +329,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     float lt = l[t];
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
-    const int64_t qpos = qw0 + 16 * t + r16;
+    const int qpos = qw0 + 16 * t + r16;
     if (qpos > qb) continue;
     const float inv = 1.f / lt;
-    const int64_t row = (int64_t)it.b * p.T + (qpos - P0);
+    const int64_t row = (int64_t)it.b * p.T + (qpos - P);
     uint16_t* dst = p.out + (row * p.hq + it.qhead) * kD + 4 * g;
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) {
@@ -275,7 +341,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     }
     if (p.lse != nullptr && g == 0) {
       const float mu = (m[t] == kNegInf) ? 0.f : m[t];
-      p.lse[((int64_t)it.b * p.hq + it.qhead) * p.T + (qpos - P0)] = (mu + __log2f(lt)) * kLn2;
+      p.lse[((int64_t)it.b * p.hq + it.qhead) * p.T + (qpos - P)] = (mu + __log2f(lt)) * kLn2;
     }
   }
 }
