@@ -296,10 +296,9 @@ int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens, 
       const int64_t qa = start_pos + (int64_t)it.qtile * kPrefillRows;
       const int64_t last = start_pos + num_tokens - 1;
       const int64_t qb = qa + kPrefillRows - 1 < last ? qa + kPrefillRows - 1 : last;
-      KeyRange r[2];
-      const int nr = prefill_key_ranges(p, it.cls, qa, qb, r);
-      int64_t tiles = 0;
-      for (int k = 0; k < nr; ++k) tiles += tiles_of(r[k]);
+      KeyRange r0, r1;
+      const int nr = prefill_key_ranges(p, it.cls, qa, qb, r0, r1);
+      const int64_t tiles = tiles_of(r0) + (nr > 1 ? tiles_of(r1) : 0);
       o[0] = it.b; o[1] = it.qhead; o[2] = it.qtile; o[3] = (int32_t)tiles;
     }
   }

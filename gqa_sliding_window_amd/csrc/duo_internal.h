@@ -153,25 +153,26 @@ __host__ __device__ inline PrefillItem prefill_item(const PrefillParams& p, int6
 struct KeyRange { int64_t lo, hi; int64_t span; };
 
 __host__ __device__ inline int prefill_key_ranges(const PrefillParams& p, int cls, int64_t qa,
-                                                  int64_t qb, KeyRange* r) {
-  int n = 0;
+                                                  int64_t qb, KeyRange& r0, KeyRange& r1) {
   if (cls == kMain) {
     const int64_t w = p.main_window;
-    r[0].lo = (w > 0) ? ((qa - w + 1) > 0 ? (qa - w + 1) : 0) : 0;
-    r[0].hi = qb;
-    r[0].span = (w > 0) ? w : 0;
+    r0.lo = (w > 0) ? ((qa - w + 1) > 0 ? (qa - w + 1) : 0) : 0;
+    r0.hi = qb;
+    r0.span = (w > 0) ? w : 0;
+    r1 = r0;
     return 1;
   }
   // streaming head: sink positions [0, sink) that are <= the query, and the
   // `recent` positions ending at the query (model card, "Why It Works").
-  if (p.sink > 0) {
-    const int64_t hi = (qb < p.sink - 1) ? qb : (int64_t)p.sink - 1;
-    r[n].lo = 0; r[n].hi = hi; r[n].span = 0; n++;
-  }
+  KeyRange sink_r{0, (qb < p.sink - 1) ? qb : (int64_t)p.sink - 1, 0};
   int64_t lo = qa - p.recent + 1;
   if (lo < p.sink) lo = p.sink;
-  if (lo <= qb) { r[n].lo = lo; r[n].hi = qb; r[n].span = p.recent; n++; }
-  return n;
+  KeyRange recent_r{lo, qb, p.recent};
+  const bool has_sink = p.sink > 0;
+  const bool has_recent = lo <= qb;
+  r0 = has_sink ? sink_r : recent_r;
+  r1 = (has_sink && has_recent) ? recent_r : r0;
+  return (has_sink ? 1 : 0) + (has_recent ? 1 : 0);
 }
 
 __host__ __device__ inline int64_t tiles_of(const KeyRange& r) {

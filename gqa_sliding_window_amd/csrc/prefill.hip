@@ -24,7 +24,12 @@
 
 namespace duo {
 
-constexpr int kPitch = kD + 8;  // LDS row pitch in bf16 elements (272 bytes)
+// LDS row pitches (bf16 elements). K rows are read 16 rows x one 16-byte
+// column per instruction (pitch = 4 dwords mod 64 banks keeps them apart);
+// V rows are read 4 rows x 32 bytes per 16-lane group by the transpose read
+// (pitch = 8 dwords mod 64 keeps those apart).
+constexpr int kPitch = kD + 8;    // K: 272 bytes
+constexpr int kVPitch = kD + 16;  // V: 288 bytes
 constexpr int kNegBig = -0x7fffffff;
 
 struct TileRange {
@@ -115,15 +120,15 @@ __device__ __forceinline__ void store_tile(uint16_t* sk, uint16_t* sv, int ld_ro
                                            const u32x4 (&stK)[4], const u32x4 (&stV)[4]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int off = (ld_row + 16 * j) * kPitch + ld_chunk * 8;
-    *reinterpret_cast<u32x4*>(sk + off) = stK[j];
-    *reinterpret_cast<u32x4*>(sv + off) = stV[j];
+    const int row = ld_row + 16 * j;
+    *reinterpret_cast<u32x4*>(sk + row * kPitch + ld_chunk * 8) = stK[j];
+    *reinterpret_cast<u32x4*>(sv + row * kVPitch + ld_chunk * 8) = stV[j];
   }
 }
 
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][kPrefillKeys * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kPrefillKeys * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kPrefillKeys * kVPitch];
 
   const PrefillItem it = prefill_item(p, blockIdx.x);
   if (!it.valid) return;
@@ -160,15 +165,15 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   TileRange rg0, rg1;
   int nt0, ntiles;
   {
-    KeyRange kr[2];
-    const int nr = prefill_key_ranges(p, it.cls, qa, qb, kr);
-    rg0 = TileRange{(int)kr[0].lo, (int)kr[0].hi, (int)kr[0].span, (int)(kr[0].lo / kPrefillKeys) * kPrefillKeys};
-    nt0 = (int)tiles_of(kr[0]);
+    KeyRange k0, k1;
+    const int nr = prefill_key_ranges(p, it.cls, qa, qb, k0, k1);
+    rg0 = TileRange{(int)k0.lo, (int)k0.hi, (int)k0.span, (int)(k0.lo / kPrefillKeys) * kPrefillKeys};
+    nt0 = (int)tiles_of(k0);
     ntiles = nt0;
     rg1 = rg0;
     if (nr > 1) {
-      rg1 = TileRange{(int)kr[1].lo, (int)kr[1].hi, (int)kr[1].span, (int)(kr[1].lo / kPrefillKeys) * kPrefillKeys};
-      ntiles += (int)tiles_of(kr[1]);
+      rg1 = TileRange{(int)k1.lo, (int)k1.hi, (int)k1.span, (int)(k1.lo / kPrefillKeys) * kPrefillKeys};
+      ntiles += (int)tiles_of(k1);
     }
   }
 
@@ -307,8 +312,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       // O^T += V^T P^T
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint16_t* v0 = &sV[buf][(32 * kk + 4 * g + (r16 >> 2)) * kPitch + 4 * (r16 & 3)];
-        const uint16_t* v1 = v0 + 16 * kPitch;
+        const uint16_t* v0 = &sV[buf][(32 * kk + 4 * g + (r16 >> 2)) * kVPitch + 4 * (r16 & 3)];
+        const uint16_t* v1 = v0 + 16 * kVPitch;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           const bf16x8 a = cat_bf16(lds_read_tr16(v0 + 16 * dt), lds_read_tr16(v1 + 16 * dt));
