@@ -183,6 +183,25 @@ def bench_chunked(torch, G, wl, timer, warmup, steps):
     return w, mask, flops, ms, attn_ms, app_ms, app_bytes
 
 
+def bench_copy(torch, timer, warmup, steps, nbytes=1 << 30):
+    """A plain device copy of a known size: the reference that scales the
+    FETCH_SIZE / WRITE_SIZE counters of the attention kernels to bytes."""
+    src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms = timer.run(lambda i: dst.copy_(src), warmup, steps)
+    return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms, "GB/s": 2 * nbytes / (ms * 1e-3) / 1e9}
+
+
+def kernel_source_hash() -> str:
+    """Hash of the prefill kernel's sources: profile counters taken for another
+    version of the kernel are not reported."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("prefill.hip", "duo_internal.h", "mfma_common.h"):
+        h.update(open(os.path.join(HERE, "gqa_sliding_window_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def cpu_baseline(w, qkv, target_s):
     """Time the float64 oracle on a bounded sample of the headline workload."""
     import threadpoolctl
@@ -214,7 +233,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sections", default="prefill,decode,chunked",
-                    help="comma list of prefill, decode, chunked")
+                    help="comma list of prefill, decode, chunked, copy (copy = counter "
+                         "calibration: a plain 1 GiB device copy)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -248,7 +268,7 @@ def main():
         traffic = None
         if os.path.exists(TRAFFIC_FILE):
             t = json.load(open(TRAFFIC_FILE)).get("prefill_kernel")
-            if t and t.get("workload") == w2.name:
+            if t and t.get("workload") == w2.name and t.get("source_hash") == kernel_source_hash():
                 traffic = t.get("bytes_per_launch")
         res["roofline"] = {"kernel": "prefill_kernel", "bound": "mfma", "achieved": tflops,
                            "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
@@ -278,6 +298,10 @@ def main():
         res["kv_append"] = {"workload": "one 8192-token chunk, 8 KV heads", "ms": app_ms,
                             "GB/s": app_bytes / (app_ms * 1e-3) / 1e9}
         log(f"chunked prefill: {ms5:.2f} ms total, attention {attn5:.2f} ms")
+
+    if "copy" in sections:
+        res["copy_reference"] = bench_copy(torch, timer, args.warmup, args.steps)
+        log(f"copy reference: {res['copy_reference']['GB/s']:.0f} GB/s")
 
     if w2 is not None and args.cpu_seconds > 0:
         log("cpu baseline: timing the oracle")
