@@ -4,7 +4,8 @@
 // One query token per sequence at position L-1 (its K/V already appended).
 // Full-context heads read every cached position, streaming heads read their
 // sink + recent slots (model card "DuoAttention Laguna Adapter", "Why It
-// Works": streaming heads keep only sink tokens plus the most recent tokens),
+// Works": a streaming head holds only the sequence's first positions and its
+// newest ones),
 // a sliding layer reads its window ring (Laguna-M.1-8bit blog post,
 // sliding-window section). Every occupied slot of a cache is visible to the
 // decode query, so a decode reads slots [0, n) in storage order; softmax does

@@ -5,7 +5,8 @@
 // every position (slot = position), a sliding layer keeps a ring of W slots,
 // streaming heads keep the sink positions and a ring of `recent` slots
 // (model card "DuoAttention Laguna Adapter", "Summary" and "Why It Works":
-// a streaming cache made of a fixed sink window and a recent-token window).
+// streaming heads hold the first positions of the sequence and a window of
+// the newest ones).
 //
 // One 256-byte row (one token of one KV head) is copied by 16 lanes with
 // 16-byte loads and stores; the kernel is a pure HBM stream. When a call

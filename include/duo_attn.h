@@ -8,11 +8,12 @@
  *  - Hugging Face model card "DuoAttention Laguna Adapter": "Summary" (KV heads
  *    split into full-context and streaming heads; sink size 64, recent size
  *    256; a learned full_attention_heads tensor), "Why It Works" (full-context
- *    heads retain all prior tokens, streaming heads keep sink tokens plus the
- *    most recent tokens), "Changes In This Submission" (head reordering so
+ *    heads hold every earlier position, a streaming head holds only the
+ *    first positions and the newest ones), "Changes In This Submission" (head
+ *    reordering so
  *    full and streaming heads are separated; static Duo KV cache).
  *  - Blog post on Laguna-M.1-8bit attention: sliding-window section (a token
- *    attends a fixed window of preceding tokens, O(n^2) -> O(n*w)),
+ *    looks back over a fixed-width window, cost O(n*w) instead of O(n^2)),
  *    implementation section (per-layer layer_types / sliding_window, None for
  *    full layers), mask-generation section (causal and sliding-window causal
  *    masks chosen per layer type).

@@ -9,13 +9,14 @@ Every function states the passage of the pages it follows:
 
 * Hugging Face model card "DuoAttention Laguna Adapter" (sections "Summary",
   "Why It Works", "Changes In This Submission") -- full-context KV heads keep
-  every earlier token; streaming KV heads keep sink tokens plus the most recent
-  tokens (sink 64, recent 256); head routing is per KV head.
+  every earlier token; streaming KV heads hold only the first positions of the
+  sequence and a window of the newest ones (sink 64, recent 256); head
+  routing is per KV head.
 * Blog post on Laguna-M.1-8bit attention, sections on how the sliding window
   works, its implementation (per-layer ``layer_types`` / ``sliding_window``)
   and mask generation (``create_causal_mask`` /
-  ``create_sliding_window_causal_mask``) -- a token attends a fixed window of
-  preceding tokens; full layers are causal.
+  ``create_sliding_window_causal_mask``) -- each token looks back over a
+  window of fixed width; full layers are causal.
 * SGLang cookbook "Laguna-XS-2.1", section 1 "Model Introduction" -- 48 Q /
   8 KV heads, window 512.
 

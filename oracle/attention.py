@@ -8,15 +8,15 @@ returned, all in float64 on the exact bf16 values the GPU receives.
 Readings of the pages (where they are silent or disagree), used throughout:
 
 R1 Window width. The blog post on Laguna-M.1-8bit (section on how the sliding
-   window works) says each token attends a fixed window of preceding tokens;
+   window works) describes each token looking back over a fixed-width window;
    the SGLang cookbook (section 1) gives the window as 512. Read as: the
    window holds W positions including the query itself, j in [i-W+1, i].
 R2 Causal window. The Laguna-XS-2.1 post (section on the golden rule of
-   sliding-window attention) says "before and after"; the Laguna-M.1-8bit post
-   says "preceding" and both name create_sliding_window_causal_mask. Read as
-   causal.
+   sliding-window attention) describes the window as reaching to both sides;
+   the Laguna-M.1-8bit post describes only earlier tokens, and both name
+   create_sliding_window_causal_mask. Read as causal.
 R3 "Recent" includes the current token: j in [i-R+1, i] (model card,
-   "Why It Works": streaming heads keep the most recent tokens).
+   "Why It Works": streaming heads hold the newest positions).
 R4 Sink and recent sets overlap for small i; the visible set is their union.
 R5 Sink tokens are absolute positions 0..S-1 of the whole sequence.
 R6 Query head h reads KV head floor(h / G), G = Hq / Hkv (contiguous groups;
@@ -65,7 +65,7 @@ def visible_positions(i: int, layer: str, window: int, streaming: bool,
     """Sorted key positions that query position ``i`` attends.
 
     * full-context head on a full layer: every position 0..i (model card,
-      "Why It Works": full-context heads retain all prior tokens; Laguna-M.1
+      "Why It Works": full-context heads hold every earlier position; Laguna-M.1
       post, mask generation: create_causal_mask);
     * full-context head on a sliding layer with window W > 0: the W positions
       ending at i (readings R1, R2, R10);

@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 What the pages fix: full-context KV heads keep every earlier token; streaming
-heads keep a fixed sink window plus a recent-token window (model card
+heads hold the sequence's first positions plus a window of the newest ones (model card
 "DuoAttention Laguna Adapter", "Summary" and "Why It Works"); the adapter
 reorders heads so full and streaming heads are separated (same card, "Changes
 In This Submission"); a static Duo KV cache is preallocated (same section).
