@@ -71,6 +71,7 @@ def load(path: str = LIB_PATH):
         "duo_decode_plan": (ctypes.c_int, [LP, i32, i64, I32P, I32P, I64P]),
         "duo_last_error": (ctypes.c_char_p, []),
         "duo_attn_version": (ctypes.c_int, []),
+        "duo_prefill_tile_rows": (ctypes.c_int, []),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -224,6 +225,10 @@ def head_plan(layer: Layer):
     cl = layer._c()
     _check(lib.duo_head_plan(ctypes.byref(cl), cls, rank, ctypes.byref(nm), ctypes.byref(ns)))
     return list(cls), list(rank), nm.value, ns.value
+
+
+def prefill_tile_rows() -> int:
+    return int(load().duo_prefill_tile_rows())
 
 
 def prefill_plan(layer: Layer, batch: int, num_tokens: int, start_pos: int = 0):

@@ -208,6 +208,8 @@ extern "C" {
 
 int duo_attn_version(void) { return DUO_ATTN_VERSION; }
 
+int duo_prefill_tile_rows(void) { return kPrefillRows; }
+
 const char* duo_last_error(void) { return g_err; }
 
 int duo_head_plan(const duo_layer* layer, int32_t* head_class, int32_t* head_rank_out, int32_t* n_main,

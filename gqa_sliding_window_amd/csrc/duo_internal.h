@@ -12,7 +12,10 @@ namespace duo {
 constexpr int kD = 128;           // head_dim
 constexpr int kMaxKv = 32;        // KV heads per layer
 constexpr int kMaxGroup = 16;     // query heads per KV head (MFMA columns)
-constexpr int kPrefillRows = 128; // query rows per prefill workgroup (4 waves x 32)
+#ifndef DUO_PREFILL_ROWS
+#define DUO_PREFILL_ROWS 128
+#endif
+constexpr int kPrefillRows = DUO_PREFILL_ROWS;  // query rows per prefill workgroup
 constexpr int kPrefillKeys = 64;  // keys per prefill K/V tile
 constexpr int kDecodeKeys = 32;   // keys per decode tile (one wave)
 constexpr int kDecodeWaves = 4;   // waves per decode workgroup
@@ -119,7 +122,7 @@ struct PrefillItem {
   int32_t b, kvh, rank, qhead, qtile;
 };
 
-// Workgroup -> work item. Units (one 128-row query tile of one KV-head group)
+// Workgroup -> work item. Units (one kPrefillRows-row query tile of one KV-head group)
 // are ordered heaviest first: main-class units before streaming units, later
 // query tiles before earlier ones. Unit u runs on XCD u % 8 (workgroups are
 // dispatched to XCDs round-robin), so every XCD gets an equal share of each

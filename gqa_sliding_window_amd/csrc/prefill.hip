@@ -31,6 +31,7 @@ namespace duo {
 constexpr int kPitch = kD + 8;    // K: 272 bytes
 constexpr int kVPitch = kD + 16;  // V: 288 bytes
 constexpr int kNegBig = -0x7fffffff;
+static_assert(kPrefillRows == 128, "the prefill kernel is written for 4 waves x 32 rows");
 
 struct TileRange {
   int lo, hi;      // visible key positions of the range (inclusive)

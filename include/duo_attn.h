@@ -181,10 +181,13 @@ int duo_head_plan(const duo_layer* layer, int32_t* head_class, int32_t* head_ran
 /* Prefill work plan (host only): the number of workgroups the prefill launch
  * uses; when `items` is not NULL it receives, per workgroup, four int32
  * (batch, q_head, q_tile, key_tiles), or (-1, -1, -1, 0) for padding, with
- * q_tile a 128-row tile of the chunk and key_tiles the 64-key tiles the
+ * q_tile a duo_prefill_tile_rows()-row tile of the chunk and key_tiles the 64-key tiles the
  * workgroup visits after masked tiles are skipped. */
 int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens,
                      int64_t start_pos, int32_t* items, int64_t* n_items);
+
+/* Query rows per prefill work item (the q_tile unit of duo_prefill_plan). */
+int duo_prefill_tile_rows(void);
 
 /* Decode work plan (host only): keys per split and number of split-K work
  * items; when `items` is not NULL it receives per item four int32

@@ -168,14 +168,15 @@ def test_prefill_plan_covers_every_tile_once_and_skips_masked(lib, case):
     L, B, T, P = case["layer"], case["B"], case["T"], case["P"]
     items = g.prefill_plan(L, B, T, P)
     real = items[items[:, 0] >= 0]
-    nqt = (T + 127) // 128
+    rows = g.prefill_tile_rows()
+    nqt = (T + rows - 1) // rows
     assert len(real) == B * L.num_q_heads * nqt
     assert len({tuple(r[:3]) for r in real}) == len(real)
     G = L.num_q_heads // L.num_kv_heads
     mask = L.full_attention_heads
     for b, h, qt, nt in real:
-        qa = P + 128 * qt
-        qb = min(qa + 127, P + T - 1)
+        qa = P + rows * qt
+        qb = min(qa + rows - 1, P + T - 1)
         streaming = mask is not None and mask[h // G] == 0
         assert nt == _expected_tiles(L, qa, qb, streaming)
     # heaviest-first per XCD: along each XCD's sequence the key-tile count never increases
