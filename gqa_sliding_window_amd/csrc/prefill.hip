@@ -77,66 +77,105 @@ __device__ __forceinline__ Src row_src(const KvSrc& s, int pos) {
   return r;
 }
 
-// Global -> registers for the tile starting at `lo` of range r: rows
-// ld_row + 16 j. Positions outside the range are clamped onto it (their
-// logits are masked; their values are finite data).
-__device__ __forceinline__ void load_tile(const KvSrc& s, const TileRange& r, int lo, int ld_row, int ld_chunk,
-                                          u32x4 (&stK)[4], u32x4 (&stV)[4]) {
+// Addressing of one tile's rows: from one base pointer and a row stride when
+// the whole tile lies in the chunk or in a stretch of the cache where
+// slot = position, else row by row (positions outside the range clamped onto
+// it: their logits are masked, their values are finite data).
+struct TileAddr {
+  const uint16_t* k;
+  const uint16_t* v;
+  int stride;     // elements between consecutive rows (fast form)
+  bool general;   // row-by-row form
+};
+
+__device__ __forceinline__ TileAddr tile_addr(const KvSrc& s, const TileRange& r, int lo) {
   const int hi = lo + kPrefillKeys - 1;
   const bool inside = lo >= r.lo && hi <= r.hi;
+  TileAddr a;
+  a.general = false;
   if (inside && lo >= s.P) {
-    // whole tile in the chunk: one base, constant row stride
-    const int64_t base = (int64_t)(lo - s.P) * s.cstride + ld_chunk * 8;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t off = base + (int64_t)(ld_row + 16 * j) * s.cstride;
-      stK[j] = *reinterpret_cast<const u32x4*>(s.ck + off);
-      stV[j] = *reinterpret_cast<const u32x4*>(s.cv + off);
-    }
-    return;
+    const int64_t off = (int64_t)(lo - s.P) * s.cstride;
+    a.k = s.ck + off;
+    a.v = s.cv + off;
+    a.stride = (int)s.cstride;
+    return a;
   }
   const bool contiguous_cache = hi < s.P && (s.cls == kStream ? hi < s.sink : s.ring_cap == 0);
   if (inside && contiguous_cache) {
-    // whole tile in a stretch of the cache where slot = position
-    const int64_t base = (int64_t)lo * kD + ld_chunk * 8;
+    const int64_t off = (int64_t)lo * kD;
+    a.k = s.mk + off;
+    a.v = s.mv + off;
+    a.stride = kD;
+    return a;
+  }
+  a.k = s.mk;
+  a.v = s.mv;
+  a.stride = 0;
+  a.general = true;
+  return a;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Direct global -> LDS loads of one K (kV = false) or V tile, this wave's
+// share. The padded LDS tile is a sequence of 16-byte slots, kSlots per row
+// (16 data columns + pad); one load instruction fills 64 consecutive slots,
+// lane l slot 64 j + l, and the tile's instructions are dealt round-robin to
+// the 4 waves. A pad slot is filled with column 0 of its row (never read).
+template <bool kV>
+__device__ __forceinline__ void dma_tile(uint16_t* lds, const KvSrc& s, const TileRange& r, int lo,
+                                         const TileAddr& ta, int wave, int lane) {
+  constexpr int kSlots = (kV ? kVPitch : kPitch) / 8;
+  constexpr int kInstr = kPrefillKeys * kSlots / 64;
+  static_assert(kPrefillKeys * kSlots % 64 == 0, "tile must be whole load instructions");
+  uint16_t* dst = lds + wave * 512;
+  if (!ta.general) {
+    const uint16_t* base = kV ? ta.v : ta.k;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t off = base + (int64_t)(ld_row + 16 * j) * kD;
-      stK[j] = *reinterpret_cast<const u32x4*>(s.mk + off);
-      stV[j] = *reinterpret_cast<const u32x4*>(s.mv + off);
+    for (int jj = 0; jj < (kInstr + 3) / 4; ++jj) {
+      const int j = wave + 4 * jj;
+      if (4 * (jj + 1) <= kInstr || j < kInstr) {
+        const int slot = 64 * j + lane;
+        const int row = slot / kSlots;
+        const int col0 = slot - row * kSlots;
+        const int col = col0 < 16 ? col0 : 0;
+        __builtin_amdgcn_global_load_lds((const void*)(base + row * ta.stride + col * 8),
+                                         (lds_void*)(dst + jj * 2048), 16, 0, 0);
+      }
     }
     return;
   }
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    int pos = lo + ld_row + 16 * j;
-    pos = pos < r.lo ? r.lo : (pos > r.hi ? r.hi : pos);
-    const Src src = row_src(s, pos);
-    stK[j] = *reinterpret_cast<const u32x4*>(src.k + ld_chunk * 8);
-    stV[j] = *reinterpret_cast<const u32x4*>(src.v + ld_chunk * 8);
-  }
-}
-
-__device__ __forceinline__ void store_tile(uint16_t* sk, uint16_t* sv, int ld_row, int ld_chunk,
-                                           const u32x4 (&stK)[4], const u32x4 (&stV)[4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = ld_row + 16 * j;
-    *reinterpret_cast<u32x4*>(sk + row * kPitch + ld_chunk * 8) = stK[j];
-    *reinterpret_cast<u32x4*>(sv + row * kVPitch + ld_chunk * 8) = stV[j];
+  for (int jj = 0; jj < (kInstr + 3) / 4; ++jj) {
+    const int j = wave + 4 * jj;
+    if (4 * (jj + 1) <= kInstr || j < kInstr) {
+      const int slot = 64 * j + lane;
+      const int row = slot / kSlots;
+      const int col0 = slot - row * kSlots;
+      const int col = col0 < 16 ? col0 : 0;
+      int pos = lo + row;
+      pos = pos < r.lo ? r.lo : (pos > r.hi ? r.hi : pos);
+      const Src rs = row_src(s, pos);
+      __builtin_amdgcn_global_load_lds((const void*)((kV ? rs.v : rs.k) + col * 8),
+                                       (lds_void*)(dst + jj * 2048), 16, 0, 0);
+    }
   }
 }
 
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][kPrefillKeys * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][kPrefillKeys * kVPitch];
+  // Two K/V buffers as separate arrays, so that loads into one are known not
+  // to alias reads of the other.
+  __shared__ __attribute__((aligned(16))) uint16_t sK0[kPrefillKeys * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sV0[kPrefillKeys * kVPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sK1[kPrefillKeys * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sV1[kPrefillKeys * kVPitch];
 
   const PrefillItem it = prefill_item(p, blockIdx.x);
   if (!it.valid) return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15;
   const int g = lane >> 4;
 
@@ -200,11 +239,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     src.mv = p.v_main + off;
   }
 
-  // ---- per-thread staging of one K/V tile: rows (tid/16) + 16 j, 16-byte chunk tid%16
-  const int ld_row = tid >> 4;
-  const int ld_chunk = tid & 15;
-  u32x4 stK[4], stV[4];
-
   // ---- running state (log2 domain: x = s * scale * log2 e)
   const float c = p.scale_log2;
   float m[2] = {kNegInf, kNegInf};
@@ -215,21 +249,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_tile(src, rg0, rg0.first, ld_row, ld_chunk, stK, stV);
-  store_tile(sK[0], sV[0], ld_row, ld_chunk, stK, stV);
-  __syncthreads();
+  auto tile_lo = [&](int idx) {
+    return idx < nt0 ? rg0.first + kPrefillKeys * idx : rg1.first + kPrefillKeys * (idx - nt0);
+  };
+  auto issue = [&](int idx, uint16_t* dk, uint16_t* dv) {
+    const TileRange& r = idx < nt0 ? rg0 : rg1;
+    const int lo = tile_lo(idx);
+    const TileAddr ta = tile_addr(src, r, lo);
+    dma_tile<false>(dk, src, r, lo, ta, wave, lane);
+    dma_tile<true>(dv, src, r, lo, ta, wave, lane);
+  };
 
-  for (int idx = 0; idx < ntiles; ++idx) {
-    const int buf = idx & 1;
-    if (idx + 1 < ntiles) {
-      const bool first_range = idx + 1 < nt0;
-      const TileRange rn = first_range ? rg0 : rg1;
-      const int lon = first_range ? rg0.first + kPrefillKeys * (idx + 1) : rg1.first + kPrefillKeys * (idx + 1 - nt0);
-      load_tile(src, rn, lon, ld_row, ld_chunk, stK, stV);
-    }
+  // One tile: start the next tile's loads into the other buffer, attend to
+  // this one, then wait for this wave's loads and meet at the barrier.
+  auto step = [&](int idx, const uint16_t* cK, const uint16_t* cV, uint16_t* nK, uint16_t* nV) {
+    if (idx + 1 < ntiles) issue(idx + 1, nK, nV);
     const bool first_range = idx < nt0;
     const TileRange r = first_range ? rg0 : rg1;
-    const int lo = first_range ? rg0.first + kPrefillKeys * idx : rg1.first + kPrefillKeys * (idx - nt0);
+    const int lo = tile_lo(idx);
     const int hi = lo + kPrefillKeys - 1;
     const bool invisible = !wave_active || lo > qw1 || (r.span > 0 && hi < qw0 - r.span + 1);
 
@@ -245,7 +282,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       for (int ds = 0; ds < 4; ++ds) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sK[buf][(16 * kt + r16) * kPitch + 32 * ds + 8 * g]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&cK[(16 * kt + r16) * kPitch + 32 * ds + 8 * g]);
           s[0][kt] = mfma_16x16x32(a, qf[0][ds], s[0][kt]);
           s[1][kt] = mfma_16x16x32(a, qf[1][ds], s[1][kt]);
         }
@@ -313,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       // O^T += V^T P^T
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint16_t* v0 = &sV[buf][(32 * kk + 4 * g + (r16 >> 2)) * kVPitch + 4 * (r16 & 3)];
+        const uint16_t* v0 = &cV[(32 * kk + 4 * g + (r16 >> 2)) * kVPitch + 4 * (r16 & 3)];
         const uint16_t* v1 = v0 + 16 * kVPitch;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
@@ -323,9 +360,17 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
         }
       }
     }
-
-    if (idx + 1 < ntiles) store_tile(sK[buf ^ 1], sV[buf ^ 1], ld_row, ld_chunk, stK, stV);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+
+  issue(0, sK0, sV0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int idx = 0; idx < ntiles; idx += 2) {
+    step(idx, sK0, sV0, sK1, sV1);
+    if (idx + 1 >= ntiles) break;
+    step(idx + 1, sK1, sV1, sK0, sV0);
   }
 
   if (!wave_active) return;
