@@ -31,7 +31,11 @@ namespace duo {
 constexpr int kPitch = kD + 8;    // K: 272 bytes
 constexpr int kVPitch = kD + 16;  // V: 288 bytes
 constexpr int kNegBig = -0x7fffffff;
-static_assert(kPrefillRows == 128, "the prefill kernel is written for 4 waves x 32 rows");
+// Query rows per wave, in 16-row MFMA column blocks (4 waves per workgroup).
+constexpr int kRT = kPrefillRows / 64;
+// (64 rows per wave would halve the LDS operand reads per MFMA, but its
+// accumulators and Q fragments do not fit one wave's registers without spills.)
+static_assert(kRT == 2, "4 waves of 32 rows");
 
 struct TileRange {
   int lo, hi;      // visible key positions of the range (inclusive)
@@ -84,8 +88,8 @@ __device__ __forceinline__ Src row_src(const KvSrc& s, int pos) {
 struct TileAddr {
   const uint16_t* k;
   const uint16_t* v;
-  int stride;     // elements between consecutive rows (fast form)
-  bool general;   // row-by-row form
+  uint32_t stride_b;  // bytes between consecutive rows (fast form)
+  bool general;       // row-by-row form
 };
 
 __device__ __forceinline__ TileAddr tile_addr(const KvSrc& s, const TileRange& r, int lo) {
@@ -97,7 +101,7 @@ __device__ __forceinline__ TileAddr tile_addr(const KvSrc& s, const TileRange& r
     const int64_t off = (int64_t)(lo - s.P) * s.cstride;
     a.k = s.ck + off;
     a.v = s.cv + off;
-    a.stride = (int)s.cstride;
+    a.stride_b = (uint32_t)s.cstride * 2u;
     return a;
   }
   const bool contiguous_cache = hi < s.P && (s.cls == kStream ? hi < s.sink : s.ring_cap == 0);
@@ -105,64 +109,78 @@ __device__ __forceinline__ TileAddr tile_addr(const KvSrc& s, const TileRange& r
     const int64_t off = (int64_t)lo * kD;
     a.k = s.mk + off;
     a.v = s.mv + off;
-    a.stride = kD;
+    a.stride_b = kD * 2u;
     return a;
   }
   a.k = s.mk;
   a.v = s.mv;
-  a.stride = 0;
+  a.stride_b = 0;
   a.general = true;
   return a;
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Direct global -> LDS loads of one K (kV = false) or V tile, this wave's
-// share. The padded LDS tile is a sequence of 16-byte slots, kSlots per row
-// (16 data columns + pad); one load instruction fills 64 consecutive slots,
-// lane l slot 64 j + l, and the tile's instructions are dealt round-robin to
-// the 4 waves. A pad slot is filled with column 0 of its row (never read).
+// Direct global -> LDS loads of a K (kV = false) or V tile. The padded LDS
+// tile is a sequence of 16-byte slots, kSlots per row (16 data columns +
+// pad); one load instruction fills 64 consecutive slots, lane l slot 64 j + l,
+// and the tile's instructions are dealt round-robin to the 4 waves. A pad
+// slot is filled with column 0 of its row (never read). The map holds, for
+// each of this wave's instructions, the tile row and the byte offset of the
+// column this lane fetches; it is the same for every tile.
+template <bool kV>
+struct SlotMap {
+  static constexpr int kSlots = (kV ? kVPitch : kPitch) / 8;
+  static constexpr int kInstr = kPrefillKeys * kSlots / 64;
+  static constexpr int kPerWave = (kInstr + 3) / 4;
+  static_assert(kPrefillKeys * kSlots % 64 == 0, "tile must be whole load instructions");
+  uint32_t row[kPerWave];
+  uint32_t colb[kPerWave];
+
+  __device__ __forceinline__ void init(int wave, int lane) {
+#pragma unroll
+    for (int jj = 0; jj < kPerWave; ++jj) {
+      const int slot = 64 * (wave + 4 * jj) + lane;
+      const int rw = slot / kSlots;
+      const int col = slot - rw * kSlots;
+      row[jj] = (uint32_t)min(rw, kPrefillKeys - 1);
+      colb[jj] = col < 16 ? (uint32_t)col * 16u : 0u;
+    }
+  }
+  __device__ __forceinline__ static bool active(int wave, int jj) {
+    return 4 * (jj + 1) <= kInstr || wave + 4 * jj < kInstr;
+  }
+};
+
 template <bool kV>
 __device__ __forceinline__ void dma_tile(uint16_t* lds, const KvSrc& s, const TileRange& r, int lo,
-                                         const TileAddr& ta, int wave, int lane) {
-  constexpr int kSlots = (kV ? kVPitch : kPitch) / 8;
-  constexpr int kInstr = kPrefillKeys * kSlots / 64;
-  static_assert(kPrefillKeys * kSlots % 64 == 0, "tile must be whole load instructions");
+                                         const TileAddr& ta, int wave, const SlotMap<kV>& map) {
   uint16_t* dst = lds + wave * 512;
   if (!ta.general) {
-    const uint16_t* base = kV ? ta.v : ta.k;
+    // uniform base + 32-bit lane offset (row < 64, stride < 2^24 bytes)
+    const char* base = reinterpret_cast<const char*>(kV ? ta.v : ta.k);
 #pragma unroll
-    for (int jj = 0; jj < (kInstr + 3) / 4; ++jj) {
-      const int j = wave + 4 * jj;
-      if (4 * (jj + 1) <= kInstr || j < kInstr) {
-        const int slot = 64 * j + lane;
-        const int row = slot / kSlots;
-        const int col0 = slot - row * kSlots;
-        const int col = col0 < 16 ? col0 : 0;
-        __builtin_amdgcn_global_load_lds((const void*)(base + row * ta.stride + col * 8),
-                                         (lds_void*)(dst + jj * 2048), 16, 0, 0);
+    for (int jj = 0; jj < SlotMap<kV>::kPerWave; ++jj) {
+      if (SlotMap<kV>::active(wave, jj)) {
+        const uint32_t off = __umul24(map.row[jj], ta.stride_b) + map.colb[jj];
+        __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void*)(dst + jj * 2048), 16, 0, 0);
       }
     }
     return;
   }
 #pragma unroll
-  for (int jj = 0; jj < (kInstr + 3) / 4; ++jj) {
-    const int j = wave + 4 * jj;
-    if (4 * (jj + 1) <= kInstr || j < kInstr) {
-      const int slot = 64 * j + lane;
-      const int row = slot / kSlots;
-      const int col0 = slot - row * kSlots;
-      const int col = col0 < 16 ? col0 : 0;
-      int pos = lo + row;
+  for (int jj = 0; jj < SlotMap<kV>::kPerWave; ++jj) {
+    if (SlotMap<kV>::active(wave, jj)) {
+      int pos = lo + (int)map.row[jj];
       pos = pos < r.lo ? r.lo : (pos > r.hi ? r.hi : pos);
       const Src rs = row_src(s, pos);
-      __builtin_amdgcn_global_load_lds((const void*)((kV ? rs.v : rs.k) + col * 8),
-                                       (lds_void*)(dst + jj * 2048), 16, 0, 0);
+      const char* src = reinterpret_cast<const char*>(kV ? rs.v : rs.k) + map.colb[jj];
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + jj * 2048), 16, 0, 0);
     }
   }
 }
 
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(256, kRT == 2 ? 2 : 1) void prefill_kernel(PrefillParams p) {
   // Two K/V buffers as separate arrays, so that loads into one are known not
   // to alias reads of the other.
   __shared__ __attribute__((aligned(16))) uint16_t sK0[kPrefillKeys * kPitch];
@@ -183,14 +201,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   const int last = P + p.T - 1;
   const int qa = P + it.qtile * kPrefillRows;
   const int qb = min(qa + kPrefillRows - 1, last);
-  const int qw0 = qa + wave * 32;
-  const int qw1 = min(qw0 + 31, qb);
+  const int qw0 = qa + wave * 16 * kRT;
+  const int qw1 = min(qw0 + 16 * kRT - 1, qb);
   const bool wave_active = qw0 <= qb;
 
   // ---- Q fragments (B operand of S^T = K Q^T): row qw0 + 16t + r16.
-  bf16x8 qf[2][4];
+  bf16x8 qf[kRT][4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < kRT; ++t) {
     const int qpos = qw0 + 16 * t + r16;
     const bool ok = qpos <= qb;
     const uint16_t* src = p.q + (((int64_t)it.b * p.T + (ok ? qpos - P : 0)) * p.hq + it.qhead) * kD + 8 * g;
@@ -241,23 +259,31 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 
   // ---- running state (log2 domain: x = s * scale * log2 e)
   const float c = p.scale_log2;
-  float m[2] = {kNegInf, kNegInf};
-  float l[2] = {0.f, 0.f};
-  f32x4 o[2][8];
+  float m[kRT], l[kRT];
+  f32x4 o[kRT][8];
 #pragma unroll
-  for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < kRT; ++t) {
+    m[t] = kNegInf;
+    l[t] = 0.f;
+  }
+#pragma unroll
+  for (int t = 0; t < kRT; ++t)
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   auto tile_lo = [&](int idx) {
     return idx < nt0 ? rg0.first + kPrefillKeys * idx : rg1.first + kPrefillKeys * (idx - nt0);
   };
+  SlotMap<false> kmap;
+  SlotMap<true> vmap;
+  kmap.init(wave, lane);
+  vmap.init(wave, lane);
   auto issue = [&](int idx, uint16_t* dk, uint16_t* dv) {
     const TileRange& r = idx < nt0 ? rg0 : rg1;
     const int lo = tile_lo(idx);
     const TileAddr ta = tile_addr(src, r, lo);
-    dma_tile<false>(dk, src, r, lo, ta, wave, lane);
-    dma_tile<true>(dv, src, r, lo, ta, wave, lane);
+    dma_tile<false>(dk, src, r, lo, ta, wave, kmap);
+    dma_tile<true>(dv, src, r, lo, ta, wave, vmap);
   };
 
   // One tile: start the next tile's loads into the other buffer, attend to
@@ -272,10 +298,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 
     if (!invisible) {
       const bool need_mask = !(lo >= r.lo && hi <= r.hi && hi <= qw0 && (r.span == 0 || lo >= qw1 - r.span + 1));
-      // S^T = K Q^T for 64 keys x 32 rows
-      f32x4 s[2][4];
+      // S^T = K Q^T for 64 keys x 16 kRT rows
+      f32x4 s[kRT][4];
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < kRT; ++t)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) s[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -283,14 +309,14 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(&cK[(16 * kt + r16) * kPitch + 32 * ds + 8 * g]);
-          s[0][kt] = mfma_16x16x32(a, qf[0][ds], s[0][kt]);
-          s[1][kt] = mfma_16x16x32(a, qf[1][ds], s[1][kt]);
+#pragma unroll
+          for (int t = 0; t < kRT; ++t) s[t][kt] = mfma_16x16x32(a, qf[t][ds], s[t][kt]);
         }
       }
       if (need_mask) {
         // row q sees keys in [klo, khi]
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < kRT; ++t) {
           const int q = qw0 + 16 * t + r16;
           const int klo = max(r.lo, r.span > 0 ? q - r.span + 1 : kNegBig);
           const int khi = min(r.hi, q);
@@ -304,22 +330,24 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
             }
         }
       }
-      // Online softmax. Each lane holds 16 logits of each of its two rows; the
+      // Online softmax. Each lane holds 16 logits of each of its rows; the
       // 4 lanes of a row share the row maximum. The maximum only moves when
       // some lane's logits exceed it by the rescale threshold, so the
       // cross-lane exchange is skipped on most tiles.
-      float lmx[2];
+      float lmx[kRT];
+      bool grow = false;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < kRT; ++t) {
         float v = fmaxf(fmaxf(s[t][0][0], s[t][0][1]), fmaxf(s[t][0][2], s[t][0][3]));
 #pragma unroll
         for (int kt = 1; kt < 4; ++kt)
           v = fmaxf(fmaxf(v, fmaxf(s[t][kt][0], s[t][kt][1])), fmaxf(s[t][kt][2], s[t][kt][3]));
         lmx[t] = v * c;
+        grow = grow || lmx[t] > m[t] + kRescaleThreshold;
       }
-      if (__any(lmx[0] > m[0] + kRescaleThreshold || lmx[1] > m[1] + kRescaleThreshold)) {
+      if (__any(grow)) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+        for (int t = 0; t < kRT; ++t) {
           float mx = wave_xor_max(lmx[t], 16);
           mx = wave_xor_max(mx, 32);
           const bool up = mx > m[t] + kRescaleThreshold;
@@ -330,9 +358,9 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
           for (int dt = 0; dt < 8; ++dt) o[t][dt] *= a;
         }
       }
-      bf16x8 pb[2][2];
+      bf16x8 pb[kRT][2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int t = 0; t < kRT; ++t) {
         const float mu = (m[t] == kNegInf) ? 0.f : m[t];
         float sum = 0.f;
 #pragma unroll
@@ -355,8 +383,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
           const bf16x8 a = cat_bf16(lds_read_tr16(v0 + 16 * dt), lds_read_tr16(v1 + 16 * dt));
-          o[0][dt] = mfma_16x16x32(a, pb[0][kk], o[0][dt]);
-          o[1][dt] = mfma_16x16x32(a, pb[1][kk], o[1][dt]);
+#pragma unroll
+          for (int t = 0; t < kRT; ++t) o[t][dt] = mfma_16x16x32(a, pb[t][kk], o[t][dt]);
         }
       }
     }
@@ -376,7 +404,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   if (!wave_active) return;
   // ---- epilogue: O = O^T / l, bf16 round-to-nearest-even; lse = (m + log2 l) ln 2
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < kRT; ++t) {
     float lt = l[t];
     lt += __shfl_xor(lt, 16);
     lt += __shfl_xor(lt, 32);
