@@ -31,7 +31,8 @@ constexpr int kTileElems = kDecodeKeys * kDPitch;  // one K or V tile in LDS
 
 // One 32-key tile, global -> registers: rows ld_row + 4 j (clamped to the
 // split's last slot), 16-byte chunk ld_chunk; each load instruction of the
-// wave covers 4 consecutive 256-byte rows.
+// wave covers 4 consecutive 256-byte rows. The cache is read once per call,
+// so the loads are non-temporal (they do not displace reused lines).
 __device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t* vbase, int64_t k0,
                                           int64_t k_end, int ld_row, int ld_chunk, u32x4 (&stK)[8],
                                           u32x4 (&stV)[8]) {
@@ -39,8 +40,8 @@ __device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t*
   for (int j = 0; j < 8; ++j) {
     int64_t slot = k0 + ld_row + 4 * j;
     slot = slot < k_end ? slot : k_end - 1;  // k_end >= 1 for a non-empty split
-    stK[j] = *reinterpret_cast<const u32x4*>(kbase + slot * kD + ld_chunk * 8);
-    stV[j] = *reinterpret_cast<const u32x4*>(vbase + slot * kD + ld_chunk * 8);
+    stK[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kbase + slot * kD + ld_chunk * 8));
+    stV[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vbase + slot * kD + ld_chunk * 8));
   }
 }
 
