@@ -208,7 +208,7 @@ def cpu_baseline(w, qkv, target_s):
     import oracle
     import workloads as wl
     q, k, v = qkv
-    rows = wl.sample_query_rows(w, w.seq, 4096)
+    rows = wl.sample_query_rows(w, w.seq, 32768)
     rng = np.random.default_rng(0)
     rows = rows[rng.permutation(len(rows))]
     done = 0
