@@ -292,7 +292,7 @@ int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens, 
   if (n_items) *n_items = nb;
   if (items) {
     for (int64_t i = 0; i < nb; ++i) {
-      const PrefillItem it = prefill_item(p, i);
+      const PrefillItem it = prefill_item(p, (int)i);
       int32_t* o = items + 4 * i;
       if (!it.valid) { o[0] = o[1] = o[2] = -1; o[3] = 0; continue; }
       const int64_t qa = start_pos + (int64_t)it.qtile * kPrefillRows;
@@ -369,7 +369,7 @@ int duo_decode_plan(const duo_layer* layer, int32_t batch, int64_t max_seq_len, 
   if (n_items) *n_items = p.n_items;
   if (items) {
     for (int64_t i = 0; i < p.n_items; ++i) {
-      const DecodeItem it = decode_item(p, i);
+      const DecodeItem it = decode_item(p, (int)i);
       int32_t* o = items + 4 * i;
       o[0] = it.b; o[1] = it.kvh; o[2] = it.split; o[3] = it.cls;
     }

@@ -151,9 +151,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
   const int G = p.group;
 
   const int64_t len = p.seq_lens[it.b];
-  const int64_t n_valid = decode_valid_slots(p, it.cls, len > 0 ? len : 0);
+  const int n_valid = (int)decode_valid_slots(p, it.cls, len > 0 ? len : 0);  // < 2^31
   const int n_planned = (it.cls == kStream) ? p.n_split_stream : p.n_split_main;
-  int n_used = (int)((n_valid + p.split_keys - 1) / p.split_keys);
+  int n_used = (n_valid + p.split_keys - 1) / p.split_keys;
   if (n_used > n_planned) n_used = n_planned;  // a length beyond the planned maximum is cut
   const int64_t k_begin = (int64_t)it.split * p.split_keys;
   int64_t k_end = k_begin + p.split_keys;

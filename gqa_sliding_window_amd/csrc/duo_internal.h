@@ -128,23 +128,25 @@ struct PrefillItem {
 // dispatched to XCDs round-robin), so every XCD gets an equal share of each
 // cost level; the `group` query heads of one unit are consecutive on that XCD
 // and share the unit's K/V tiles through its L2.
-__host__ __device__ inline PrefillItem prefill_item(const PrefillParams& p, int64_t block) {
+// (32-bit arithmetic: the host keeps grids below 2^31 workgroups; a 64-bit
+// division would run as a long software sequence in every workgroup.)
+__host__ __device__ inline PrefillItem prefill_item(const PrefillParams& p, int block) {
   PrefillItem it{};
-  const int64_t x = block % kXcds;
-  const int64_t s = block / kXcds;
-  const int64_t unit = (s / p.group) * kXcds + x;
-  const int g = (int)(s % p.group);
+  const int x = block % kXcds;
+  const int s = block / kXcds;
+  const int unit = (s / p.group) * kXcds + x;
+  const int g = s % p.group;
   if (unit >= p.n_units) { it.valid = 0; return it; }
   it.valid = 1;
-  int64_t u = unit;
+  int u = unit;
   int n_class = p.n_main;
   it.cls = kMain;
   if (u >= p.n_units_main) { u -= p.n_units_main; it.cls = kStream; n_class = p.n_stream; }
-  const int64_t groups = (int64_t)p.batch * n_class;
-  it.qtile = p.n_qtiles - 1 - (int)(u / groups);
-  const int64_t grp = u % groups;
-  it.b = (int)(grp / n_class);
-  it.rank = (int)(grp % n_class);
+  const int groups = p.batch * n_class;
+  it.qtile = p.n_qtiles - 1 - u / groups;
+  const int grp = u % groups;
+  it.b = grp / n_class;
+  it.rank = grp % n_class;
   it.kvh = class_head(p.stream_mask, p.hkv, it.cls, it.rank);
   it.qhead = it.kvh * p.group + g;
   return it;
@@ -211,15 +213,15 @@ struct DecodeItem { int32_t cls, b, rank, kvh, split; };
 
 // Work item i: main-class items (batch, head rank, split) first, then
 // streaming items.
-__host__ __device__ inline DecodeItem decode_item(const DecodeParams& p, int64_t i) {
+__host__ __device__ inline DecodeItem decode_item(const DecodeParams& p, int i) {
   DecodeItem it{};
   int ns = p.n_split_main, nc = p.n_main;
   it.cls = kMain;
   if (i >= p.n_items_main) { i -= p.n_items_main; it.cls = kStream; ns = p.n_split_stream; nc = p.n_stream; }
-  it.split = (int)(i % ns);
-  const int64_t bh = i / ns;
-  it.b = (int)(bh / nc);
-  it.rank = (int)(bh % nc);
+  it.split = i % ns;
+  const int bh = i / ns;
+  it.b = bh / nc;
+  it.rank = bh % nc;
   it.kvh = class_head(p.stream_mask, p.hkv, it.cls, it.rank);
   return it;
 }
