@@ -31,11 +31,13 @@ namespace duo {
 constexpr int kPitch = kD + 8;    // K: 272 bytes
 constexpr int kVPitch = kD + 16;  // V: 288 bytes
 constexpr int kNegBig = -0x7fffffff;
-// Query rows per wave, in 16-row MFMA column blocks (4 waves per workgroup).
-constexpr int kRT = kPrefillRows / 64;
-// (64 rows per wave would halve the LDS operand reads per MFMA, but its
+// Query rows per wave, in 16-row MFMA column blocks: 32 rows per wave. (64
+// rows per wave would halve the LDS operand reads per MFMA, but its
 // accumulators and Q fragments do not fit one wave's registers without spills.)
-static_assert(kRT == 2, "4 waves of 32 rows");
+constexpr int kRT = 2;
+constexpr int kWaves = kPrefillRows / (16 * kRT);  // waves per workgroup
+constexpr int kThreads = 64 * kWaves;
+static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves of 32 rows");
 
 struct TileRange {
   int lo, hi;      // visible key positions of the range (inclusive)
@@ -124,7 +126,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // Direct global -> LDS loads of a K (kV = false) or V tile. The padded LDS
 // tile is a sequence of 16-byte slots, kSlots per row (16 data columns +
 // pad); one load instruction fills 64 consecutive slots, lane l slot 64 j + l,
-// and the tile's instructions are dealt round-robin to the 4 waves. A pad
+// and the tile's instructions are dealt round-robin to the waves. A pad
 // slot is filled with column 0 of its row (never read). The map holds, for
 // each of this wave's instructions, the tile row and the byte offset of the
 // column this lane fetches; it is the same for every tile.
@@ -132,7 +134,7 @@ template <bool kV>
 struct SlotMap {
   static constexpr int kSlots = (kV ? kVPitch : kPitch) / 8;
   static constexpr int kInstr = kPrefillKeys * kSlots / 64;
-  static constexpr int kPerWave = (kInstr + 3) / 4;
+  static constexpr int kPerWave = (kInstr + kWaves - 1) / kWaves;
   static_assert(kPrefillKeys * kSlots % 64 == 0, "tile must be whole load instructions");
   uint32_t row[kPerWave];
   uint32_t colb[kPerWave];
@@ -140,7 +142,7 @@ struct SlotMap {
   __device__ __forceinline__ void init(int wave, int lane) {
 #pragma unroll
     for (int jj = 0; jj < kPerWave; ++jj) {
-      const int slot = 64 * (wave + 4 * jj) + lane;
+      const int slot = 64 * (wave + kWaves * jj) + lane;
       const int rw = slot / kSlots;
       const int col = slot - rw * kSlots;
       row[jj] = (uint32_t)min(rw, kPrefillKeys - 1);
@@ -148,7 +150,7 @@ struct SlotMap {
     }
   }
   __device__ __forceinline__ static bool active(int wave, int jj) {
-    return 4 * (jj + 1) <= kInstr || wave + 4 * jj < kInstr;
+    return kWaves * (jj + 1) <= kInstr || wave + kWaves * jj < kInstr;
   }
 };
 
@@ -163,7 +165,7 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const KvSrc& s, const Ti
     for (int jj = 0; jj < SlotMap<kV>::kPerWave; ++jj) {
       if (SlotMap<kV>::active(wave, jj)) {
         const uint32_t off = __umul24(map.row[jj], ta.stride_b) + map.colb[jj];
-        __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void*)(dst + jj * 2048), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void*)(dst + jj * 512 * kWaves), 16, 0, 0);
       }
     }
     return;
@@ -175,12 +177,12 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const KvSrc& s, const Ti
       pos = pos < r.lo ? r.lo : (pos > r.hi ? r.hi : pos);
       const Src rs = row_src(s, pos);
       const char* src = reinterpret_cast<const char*>(kV ? rs.v : rs.k) + map.colb[jj];
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + jj * 2048), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + jj * 512 * kWaves), 16, 0, 0);
     }
   }
 }
 
-__global__ __launch_bounds__(256, kRT == 2 ? 2 : 1) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillParams p) {
   // Two K/V buffers as separate arrays, so that loads into one are known not
   // to alias reads of the other.
   __shared__ __attribute__((aligned(16))) uint16_t sK0[kPrefillKeys * kPitch];
@@ -426,7 +428,7 @@ __global__ __launch_bounds__(256, kRT == 2 ? 2 : 1) void prefill_kernel(PrefillP
 }
 
 hipError_t launch_prefill(const PrefillParams& p, int64_t n_blocks, hipStream_t s) {
-  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)n_blocks), dim3(256), 0, s, p);
+  hipLaunchKernelGGL(prefill_kernel, dim3((unsigned)n_blocks), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
