@@ -7,7 +7,9 @@
 * parity within max-abs 2e-2 / mean-abs 2e-3 on every row of small and ragged
   cases, the sliding-window prefill workload (batch 1, 12/2 heads, 1024
   tokens, window 512) and chunked Duo prefill, and on 4096 seeded sampled rows
-  of the full-attention prefill workload (batch 4, 48/8 heads, 8192 tokens).
+  of the full-attention prefill workload (batch 4, 48/8 heads, 8192 tokens)
+  and of the DuoAttention long-context chunked prefill (131072 tokens in
+  8192-token chunks, attend then append, as the benchmark runs it).
 """
 import math
 
@@ -175,4 +177,22 @@ def test_full_prefill_workload_sampled(lib):
     out, lse = run_chunked(lib, layer, q, k, v, w.seq)
     rows = wl.sample_query_rows(w, w.seq, w.oracle_rows,
                                 must=(0, 63, 64, 127, 128, 255, 256, 319, 320, 511, 512, 8191))
+    compare_rows(layer, q, k, v, out, lse, rows, w.name)
+
+
+def test_duo_chunked_prefill_workload_sampled(lib):
+    """DuoAttention long-context chunked prefill at full size: batch 1, 131072
+    tokens in 16 chunks of 8192 (attend, then append), 48/8 heads, the seeded
+    Bernoulli(0.25) head mask; 4096 seeded rows including the first and last
+    row of every chunk and the sink / recent edges."""
+    w = wl.WORKLOADS[5]
+    mask = wl.duo_mask(w).tolist()
+    announce(f"prefill parity {w.name} mask {mask}")
+    layer = lib.Layer(full_attention_heads=mask)
+    q, k, v = _gen(w.seed, w.batch, w.seq, w.hq, w.hkv)
+    out, lse = run_chunked(lib, layer, q, k, v, w.chunk)
+    rows = wl.sample_query_rows(w, w.seq, w.oracle_rows, chunk=w.chunk,
+                                must=(63, 64, 255, 256, 319, 320, 321, 8191 + 320, w.seq - 1))
+    G = w.hq // w.hkv
+    rows = rows[np.lexsort((rows[:, 2], rows[:, 1] // G, rows[:, 0]))]  # one K/V head at a time
     compare_rows(layer, q, k, v, out, lse, rows, w.name)
