@@ -46,10 +46,14 @@ def log(msg):
 
 class Timer:
     """HIP-event timing on torch's current stream (the stream the library
-    launches on)."""
+    launches on). The mean comes from one event pair around K back-to-back
+    calls; a second pass of K calls with an event between consecutive calls
+    gives the per-call median and minimum (events between calls slow short
+    kernels slightly, so they stay out of the mean)."""
 
     def __init__(self, torch):
         self.torch = torch
+        self.last = {}
 
     def run(self, fn, warmup, steps):
         torch = self.torch
@@ -64,7 +68,16 @@ class Timer:
             fn(warmup + i)
         e1.record(s)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / steps  # ms per call
+        mean = e0.elapsed_time(e1) / steps  # ms per call
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        ev[0].record(s)
+        for i in range(steps):
+            fn(warmup + steps + i)
+            ev[i + 1].record(s)
+        torch.cuda.synchronize()
+        per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        self.last = {"median_ms": per[len(per) // 2], "min_ms": per[0]}
+        return mean
 
 
 def dev_bits(torch, bits):
@@ -167,6 +180,7 @@ def bench_chunked(torch, G, wl, timer, warmup, steps):
 
     log("chunked prefill: timing passes")
     ms = timer.run(one_pass, warmup, steps)
+    pass_stats = dict(timer.last)
     # attention-only: per-chunk prefill calls alone, cache already filled
     s = torch.cuda.current_stream()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_chunks)]
@@ -180,7 +194,7 @@ def bench_chunked(torch, G, wl, timer, warmup, steps):
     # cache manager on one chunk: read 2 x chunk rows, write 2 x chunk rows
     app_ms = timer.run(lambda i: G.kv_append(layer, cache, k[0], v[0], starts[0], max_end_pos=w.chunk), 2, 20)
     app_bytes = 2 * 2 * w.chunk * w.hkv * 128 * 2
-    return w, mask, flops, ms, attn_ms, app_ms, app_bytes
+    return w, mask, flops, ms, attn_ms, app_ms, app_bytes, pass_stats
 
 
 def bench_copy(torch, timer, warmup, steps, nbytes=1 << 30):
@@ -202,19 +216,22 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(w, qkv, target_s):
-    """Time the float64 oracle on a bounded sample of the headline workload."""
+def cpu_baseline(w, qkv, target_s, total_flop):
+    """Time the float64 oracle on a bounded sample of the headline workload
+    on one host thread (its per-row products are too small to gain from BLAS
+    threads: 16 threads measured slower than one)."""
     import threadpoolctl
     import oracle
     import workloads as wl
     q, k, v = qkv
+    threads = 1
     rows = wl.sample_query_rows(w, w.seq, 32768)
     rng = np.random.default_rng(0)
     rows = rows[rng.permutation(len(rows))]
     done = 0
     flops = 0
     t0 = time.perf_counter()
-    with threadpoolctl.threadpool_limits(1):
+    with threadpoolctl.threadpool_limits(threads):
         while done < len(rows) and time.perf_counter() - t0 < target_s:
             batch = rows[done:done + 64]
             batch = batch[np.lexsort((batch[:, 2], batch[:, 1], batch[:, 0]))]
@@ -222,9 +239,11 @@ def cpu_baseline(w, qkv, target_s):
             flops += int(4 * 128 * (batch[:, 2] + 1).sum())
             done += len(batch)
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} seeded query rows of the headline workload (float64, one thread), "
-                      f"{dt:.1f} s", "rows_per_s": done / dt}
+    rate = flops / dt
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} seeded query rows of the headline workload (float64, {threads} "
+                      f"thread), {dt:.1f} s", "rows_per_s": done / dt,
+            "extrapolated_full_workload_s": total_flop / rate}
 
 
 def main():
@@ -262,6 +281,8 @@ def main():
         tflops = flops / (ms * 1e-3) / 1e12
         res["value"] = tflops
         res["ms_per_step"] = ms
+        res["ms_per_step_median"] = timer.last["median_ms"]
+        res["ms_per_step_min"] = timer.last["min_ms"]
         res["config"] = {"workload": w2.name, "batch": w2.batch, "seq_len": w2.seq, "q_heads": w2.hq,
                          "kv_heads": w2.hkv, "head_dim": 128, "layer": "full causal",
                          "algorithmic_flop_per_step": flops}
@@ -280,19 +301,23 @@ def main():
         w3, nb3, ms3, rep3 = bench_decode_sliding(torch, G, wl, timer, args.warmup, args.steps)
         gbs3 = nb3 / (ms3 * 1e-3) / 1e9
         d["sliding_window"] = {"workload": w3.name, "kv_bytes": nb3, "ms": ms3, "GB/s": gbs3,
-                               "frac_hbm_peak": gbs3 / PEAK_HBM_GBS, "cache_replicas": rep3}
+                               "frac_hbm_peak": gbs3 / PEAK_HBM_GBS, "cache_replicas": rep3,
+                               "ms_median": timer.last["median_ms"], "ms_min": timer.last["min_ms"]}
         log(f"decode sliding: {ms3 * 1e3:.1f} us, {gbs3:.0f} GB/s")
         w4, nb4, ms4, rep4, mask4, sumL = bench_decode_duo(torch, G, wl, timer, args.warmup, args.steps)
         gbs4 = nb4 / (ms4 * 1e-3) / 1e9
         d["duo"] = {"workload": w4.name, "mask": mask4, "sum_context": sumL, "kv_bytes": nb4, "ms": ms4,
-                    "GB/s": gbs4, "frac_hbm_peak": gbs4 / PEAK_HBM_GBS, "cache_replicas": rep4}
+                    "GB/s": gbs4, "frac_hbm_peak": gbs4 / PEAK_HBM_GBS, "cache_replicas": rep4,
+                    "ms_median": timer.last["median_ms"], "ms_min": timer.last["min_ms"]}
         log(f"decode duo: {ms4 * 1e3:.1f} us, {gbs4:.0f} GB/s")
         res["decode"] = d
 
     if "chunked" in sections:
-        w5, mask5, fl5, ms5, attn5, app_ms, app_bytes = bench_chunked(torch, G, wl, timer, 1, max(1, args.steps // 10))
+        w5, mask5, fl5, ms5, attn5, app_ms, app_bytes, st5 = bench_chunked(torch, G, wl, timer, 1,
+                                                                          max(1, args.steps // 10))
         res["chunked_prefill"] = {"workload": w5.name, "mask": mask5, "algorithmic_flop": fl5,
                                   "ms_total": ms5, "TFLOP/s": fl5 / (ms5 * 1e-3) / 1e12,
+                                  "ms_total_median": st5["median_ms"], "ms_total_min": st5["min_ms"],
                                   "attention_only_ms": attn5,
                                   "attention_only_TFLOP/s": fl5 / (attn5 * 1e-3) / 1e12}
         res["kv_append"] = {"workload": "one 8192-token chunk, 8 KV heads", "ms": app_ms,
@@ -305,7 +330,7 @@ def main():
 
     if w2 is not None and args.cpu_seconds > 0:
         log("cpu baseline: timing the oracle")
-        res["cpu_baseline"] = cpu_baseline(w2, qkv, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w2, qkv, args.cpu_seconds, res["config"]["algorithmic_flop_per_step"])
     print(json.dumps(res), flush=True)
 
 
