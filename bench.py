@@ -19,7 +19,10 @@ HBM):
                  them;
   chunked_prefill -- DuoAttention prefill of 131072 tokens in 8192-token
                  chunks (attend + append per chunk);
-  kv_append   -- the cache manager on one 8192-token chunk.
+  kv_append   -- the cache manager on one 8192-token chunk;
+  kv_cache    -- static-cache footprint and occupancy of the two Duo
+                 workloads beside the same layer without Duo routing
+                 (host-side accounting).
 `roofline` describes the dominant kernel (the prefill kernel). `cpu_baseline`
 times the float64 oracle on a bounded sample of the headline workload.
 """
@@ -206,6 +209,28 @@ def bench_copy(torch, timer, warmup, steps, nbytes=1 << 30):
     return {"bytes_read": nbytes, "bytes_written": nbytes, "ms": ms, "GB/s": 2 * nbytes / (ms * 1e-3) / 1e9}
 
 
+def kv_cache_section(G, wl):
+    """Static-cache footprint of the two Duo workloads beside the same layer
+    without Duo routing (host-side accounting, no GPU time)."""
+    out = {}
+    for idx in (4, 5):
+        w = wl.WORKLOADS[idx]
+        mask = wl.duo_mask(w).tolist()
+        layer = G.Layer(full_attention_heads=mask)
+        if w.kind == "decode":
+            cap, L = w.len_hi, wl.context_lengths(w)
+        else:
+            cap, L = w.seq, np.array([w.seq] * w.batch)
+        r = G.kv_cache_report(layer, w.batch, cap, L)
+        duo = r["main_bytes"] + r["stream_bytes"]
+        out[w.name] = {"mask": mask, "capacity": cap, "duo_bytes": duo, "base_bytes": r["base_bytes"],
+                       "duo_over_base": duo / r["base_bytes"],
+                       "occupied_over_allocated": (r["main_active"] + r["stream_active"]) /
+                                                  (r["main_slots"] + r["stream_slots"]),
+                       "base_occupied_over_allocated": r["base_active"] / r["base_slots"]}
+    return out
+
+
 def kernel_source_hash() -> str:
     """Hash of the prefill kernel's sources: profile counters taken for another
     version of the kernel are not reported."""
@@ -323,6 +348,9 @@ def main():
         res["kv_append"] = {"workload": "one 8192-token chunk, 8 KV heads", "ms": app_ms,
                             "GB/s": app_bytes / (app_ms * 1e-3) / 1e9}
         log(f"chunked prefill: {ms5:.2f} ms total, attention {attn5:.2f} ms")
+
+    if "decode" in sections or "chunked" in sections:
+        res["kv_cache"] = kv_cache_section(G, wl)
 
     if "copy" in sections:
         res["copy_reference"] = bench_copy(torch, timer, args.warmup, args.steps)

@@ -66,6 +66,7 @@ def load(path: str = LIB_PATH):
         "duo_attn_decode_workspace_bytes": (sz, [LP, i32, i64]),
         "duo_attn_decode_workspace_init": (ctypes.c_int, [P, sz, P]),
         "duo_kv_cache_bytes": (ctypes.c_int, [LP, i32, i64, I64P, I64P]),
+        "duo_kv_cache_report": (ctypes.c_int, [LP, i32, i64, I32P, ctypes.POINTER(_CacheReport)]),
         "duo_head_plan": (ctypes.c_int, [LP, I32P, I32P, I32P, I32P]),
         "duo_prefill_plan": (ctypes.c_int, [LP, i32, i32, i64, I32P, I64P]),
         "duo_decode_plan": (ctypes.c_int, [LP, i32, i64, I32P, I32P, I64P]),
@@ -263,6 +264,27 @@ def kv_cache_bytes(layer: Layer, batch: int, capacity: int):
     a, b = ctypes.c_int64(), ctypes.c_int64()
     _check(lib.duo_kv_cache_bytes(ctypes.byref(cl), batch, capacity, ctypes.byref(a), ctypes.byref(b)))
     return a.value, b.value
+
+
+class _CacheReport(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in (
+        "main_slots", "stream_slots", "main_active", "stream_active", "main_bytes", "stream_bytes",
+        "base_slots", "base_active", "base_bytes")]
+
+
+def kv_cache_report(layer: Layer, batch: int, capacity: int, seq_lens) -> dict:
+    """Allocated / occupied slots and K+V bytes per head class for host
+    lengths seq_lens[batch], beside the same layer without Duo routing."""
+    import numpy as np
+    lib = load()
+    cl = layer._c()
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    if lens.shape != (batch,):
+        raise ValueError("seq_lens must have shape (batch,)")
+    rep = _CacheReport()
+    _check(lib.duo_kv_cache_report(ctypes.byref(cl), batch, capacity,
+                                   lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(rep)))
+    return {n: getattr(rep, n) for n, _ in _CacheReport._fields_}
 
 
 def prefill_flops(layer: Layer, batch: int, num_tokens: int, start_pos: int = 0) -> int:

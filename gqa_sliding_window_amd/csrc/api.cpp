@@ -240,6 +240,32 @@ int duo_kv_cache_bytes(const duo_layer* layer, int32_t batch, int64_t capacity, 
   return ok();
 }
 
+int duo_kv_cache_report(const duo_layer* layer, int32_t batch, int64_t capacity, const int32_t* seq_lens,
+                        duo_cache_report* out) {
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  if (batch < 0 || capacity < 0) return fail(DUO_ERR_INVALID_ARG, "batch and capacity must be >= 0");
+  if (out == nullptr || (batch > 0 && seq_lens == nullptr)) return fail(DUO_ERR_INVALID_ARG, "NULL argument");
+  const int64_t main_per_head = L.main_ring ? L.window : capacity;
+  const int64_t stream_per_head = (int64_t)L.sink + L.recent;
+  const int64_t slot_bytes = 2 * kD * 2;  // K and V rows of one slot
+  std::memset(out, 0, sizeof(*out));
+  out->main_slots = (int64_t)batch * L.plan.n_main * main_per_head;
+  out->stream_slots = (int64_t)batch * L.plan.n_stream * stream_per_head;
+  out->base_slots = (int64_t)batch * L.hkv * main_per_head;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t len = seq_lens[b] > 0 ? seq_lens[b] : 0;
+    out->main_active += L.plan.n_main * std::min(len, main_per_head);
+    out->stream_active += L.plan.n_stream * std::min(len, stream_per_head);
+    out->base_active += L.hkv * std::min(len, main_per_head);
+  }
+  out->main_bytes = out->main_slots * slot_bytes;
+  out->stream_bytes = out->stream_slots * slot_bytes;
+  out->base_bytes = out->base_slots * slot_bytes;
+  return ok();
+}
+
 int duo_kv_append(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch, const void* k_new,
                   const void* v_new, int32_t num_tokens, const int32_t* start_pos, int64_t max_end_pos,
                   void* stream) {

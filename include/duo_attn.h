@@ -173,6 +173,25 @@ size_t duo_attn_decode_workspace_bytes(const duo_layer* layer, int32_t batch,
 int duo_kv_cache_bytes(const duo_layer* layer, int32_t batch, int64_t capacity,
                        int64_t* main_bytes, int64_t* stream_bytes);
 
+/* Static-cache footprint and occupancy for sequences of the given lengths
+ * (HOST array seq_lens[batch]), per head class, beside the same layer without
+ * Duo routing (every KV head keeps its whole context). Host only, no GPU.
+ * Model card "DuoAttention Laguna Adapter": "Benefits" (smaller KV-cache
+ * footprint), "Changes In This Submission" (a static Duo KV cache).
+ * Bytes count K and V together (2 x 128 bf16 per slot and head). Slots are
+ * (sequence, head, slot) triples; a slot is occupied when duo_kv_append has
+ * written a position there: min(len, slots per head) per sequence and head. */
+typedef struct duo_cache_report {
+  int64_t main_slots, stream_slots;     /* allocated, per class */
+  int64_t main_active, stream_active;   /* occupied, per class */
+  int64_t main_bytes, stream_bytes;     /* allocated K+V bytes, per class */
+  int64_t base_slots, base_active;      /* the same layer with every head full context */
+  int64_t base_bytes;
+} duo_cache_report;
+
+int duo_kv_cache_report(const duo_layer* layer, int32_t batch, int64_t capacity,
+                        const int32_t* seq_lens, duo_cache_report* out);
+
 /* Head-class plan (host only, no GPU): for each KV head, its class
  * (1 = streaming, 0 = full context) and its rank within the class. */
 int duo_head_plan(const duo_layer* layer, int32_t* head_class, int32_t* head_rank,

@@ -53,3 +53,49 @@ def test_head_ranks_are_ascending_per_class():
                            full_attention_heads=[0, 1, 1, 0, 0, 1, 0, 0])
     assert c.rank == [0, 0, 1, 1, 2, 2, 3, 4]
     assert (c.n_full, c.n_stream) == (3, 5)
+
+
+# ---------------------------------------------------------------- cache report
+def _report_case(layer_kw, B, cap, lens):
+    import gqa_sliding_window_amd as g
+    L = g.Layer(**layer_kw)
+    return L, g.kv_cache_report(L, B, cap, lens)
+
+
+def test_cache_report_closed_forms(lib):
+    """Duo decode workload shape: batch 16, one full head of 8, 131072-slot
+    full cache; streaming heads hold sink 64 + recent 256 (model card,
+    "Summary"); the base layer keeps every head's whole context."""
+    lens = [32768 + 6000 * i for i in range(16)]
+    L, r = _report_case(dict(full_attention_heads=[1, 0, 0, 0, 0, 0, 0, 0]), 16, 131072, lens)
+    slot = 2 * 128 * 2
+    assert r["main_slots"] == 16 * 1 * 131072 and r["stream_slots"] == 16 * 7 * 320
+    assert r["main_bytes"] == 16 * 131072 * slot == 1073741824
+    assert r["stream_bytes"] == 16 * 7 * 320 * slot == 18350080
+    assert r["base_bytes"] == 16 * 8 * 131072 * slot == 8589934592
+    assert r["main_active"] == sum(lens) and r["stream_active"] == 16 * 7 * 320
+    assert r["base_active"] == 8 * sum(lens)
+    # sliding layer: every head is a window ring; Duo streaming heads are smaller still
+    L, r = _report_case(dict(kind=1, window=512, full_attention_heads=[1, 1, 0, 0, 0, 0, 0, 0]), 2, 0, [100, 5000])
+    assert r["main_slots"] == 2 * 2 * 512 and r["stream_slots"] == 2 * 6 * 320
+    assert r["main_active"] == 2 * (100 + 512) and r["stream_active"] == 6 * (100 + 320)
+    assert r["base_slots"] == 2 * 8 * 512 and r["base_active"] == 8 * (100 + 512)
+
+
+@pytest.mark.parametrize("mask,kind,window,cap", [
+    ([1, 0, 0, 1], 0, 0, 900), ([0, 0, 0, 0], 0, 0, 50), ([1, 0, 1, 0], 1, 40, 0)])
+def test_cache_report_occupancy_matches_shadow_model(lib, mask, kind, window, cap):
+    """Occupied slots equal the slots the token-by-token shadow model has
+    written after appending positions [0, len) of every sequence."""
+    lens = [0, 1, 63, 64, 65, 300, 321, 700]
+    B = len(lens)
+    L, r = _report_case(dict(num_q_heads=8, num_kv_heads=4, kind=kind, window=window, sink=5,
+                             recent=17, full_attention_heads=mask), B, cap, lens)
+    sc = oracle.ShadowCache(batch=B, hkv=4, layer="sliding" if kind == 1 else "full", window=window, sink=5,
+                     recent=17, full_attention_heads=mask)
+    for b, n in enumerate(lens):
+        sc.append(b, 0, n)
+    occ = {0: 0, 1: 0}
+    for (b, cls, rank), slots in sc.slots.items():
+        occ[cls] += len(slots)
+    assert (r["main_active"], r["stream_active"]) == (occ[0], occ[1])
