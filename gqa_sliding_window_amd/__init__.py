@@ -64,6 +64,8 @@ def load(path: str = LIB_PATH):
         "duo_attn_prefill": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, i64, P, P, P]),
         "duo_attn_decode": (ctypes.c_int, [LP, CP, i32, P, P, i64, P, P, P, sz, P]),
         "duo_attn_decode_workspace_bytes": (sz, [LP, i32, i64]),
+        "duo_attn_decode_block": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, P, i64, P, P, P, sz, P]),
+        "duo_attn_decode_block_workspace_bytes": (sz, [LP, i32, i32, i64]),
         "duo_attn_decode_workspace_init": (ctypes.c_int, [P, sz, P]),
         "duo_kv_cache_bytes": (ctypes.c_int, [LP, i32, i64, I64P, I64P]),
         "duo_kv_cache_report": (ctypes.c_int, [LP, i32, i64, I32P, ctypes.POINTER(_CacheReport)]),
@@ -216,6 +218,34 @@ def attn_decode(layer: Layer, cache: KVCache, q, seq_lens, max_seq_len: int, out
     _check(lib.duo_attn_decode(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(q), _ptr(seq_lens),
                                int(max_seq_len), _ptr(out), _ptr(lse), _ptr(workspace), nbytes,
                                _stream(stream)))
+
+
+def decode_block_workspace_bytes(layer: Layer, batch: int, num_tokens: int, max_past_len: int) -> int:
+    cl = layer._c()
+    return int(load().duo_attn_decode_block_workspace_bytes(ctypes.byref(cl), batch, int(num_tokens),
+                                                            int(max_past_len)))
+
+
+def decode_block_workspace(layer: Layer, batch: int, num_tokens: int, max_past_len: int, device="cuda"):
+    """A zero-filled block-decode workspace."""
+    import torch
+    n = (decode_block_workspace_bytes(layer, batch, num_tokens, max_past_len) + 3) // 4
+    ws = torch.empty(max(n, 64), dtype=torch.float32, device=device)
+    init_decode_workspace(ws)
+    return ws
+
+
+def attn_decode_block(layer: Layer, cache: KVCache, q, k_new, v_new, past_lens, max_past_len: int, out,
+                      workspace, lse=None, stream=None):
+    """duo_attn_decode_block: q/out [B, T, Hq, 128], k_new/v_new [B, T, Hkv, 128],
+    past_lens int32 [B] (device): cached positions before the block."""
+    lib = load()
+    B, T = q.shape[0], q.shape[1]
+    cl, cc = layer._c(), cache._c()
+    nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.duo_attn_decode_block(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(q), _ptr(k_new), _ptr(v_new),
+                                     T, _ptr(past_lens), int(max_past_len), _ptr(out), _ptr(lse),
+                                     _ptr(workspace), nbytes, _stream(stream)))
 
 
 def head_plan(layer: Layer):

@@ -32,6 +32,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 constexpr int64_t kMaxPos = 0x7FFFFFFF;   // positions are int32 on the device side
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // workgroups per launch
+constexpr int32_t kMaxBlockTokens = 64;   // query tokens per sequence of a block decode
 
 struct Layer {
   int hq, hkv, group, kind, window, sink, recent;
@@ -145,7 +146,11 @@ int build_prefill(const Layer& L, int32_t batch, int32_t T, int64_t start_pos, P
 // kDecodeTargetItems workgroups, a multiple of one tile per wave, never fewer
 // than kDecodeMinSplit keys and never more than kDecodeMaxSplits splits of one
 // sequence.
-int build_decode(const Layer& L, int32_t batch, int64_t max_seq_len, int64_t main_cap, DecodeParams* p) {
+// block_tokens = 0: single-token decode (the query's K/V already in the
+// cache); > 0: block decode of that many tokens after the max_seq_len cached
+// positions (their K/V read from the call's inputs).
+int build_decode(const Layer& L, int32_t batch, int64_t max_seq_len, int64_t main_cap, DecodeParams* p,
+                 int32_t block_tokens = 0) {
   std::memset(p, 0, sizeof(*p));
   p->batch = batch;
   p->hq = L.hq;
@@ -159,9 +164,13 @@ int build_decode(const Layer& L, int32_t batch, int64_t max_seq_len, int64_t mai
   p->n_stream = L.plan.n_stream;
   p->stream_mask = L.plan.stream_mask;
   p->scale_log2 = L.scale * 1.4426950408889634f;
-  const int64_t keys_main = L.main_ring ? (max_seq_len < L.window ? max_seq_len : L.window) : max_seq_len;
+  p->window = L.main_ring ? L.window : 0;
+  p->T = block_tokens > 0 ? block_tokens : 1;
+  p->n_cb = (p->T * L.group + 15) / 16;
+  const int64_t extra = block_tokens;  // the block's own keys follow the cached ones
+  const int64_t keys_main = (L.main_ring ? (max_seq_len < L.window ? max_seq_len : L.window) : max_seq_len) + extra;
   const int64_t sr = (int64_t)L.sink + L.recent;
-  const int64_t keys_stream = max_seq_len < sr ? max_seq_len : sr;
+  const int64_t keys_stream = (max_seq_len < sr ? max_seq_len : sr) + extra;
   const int64_t total = (int64_t)batch * (L.plan.n_main * keys_main + L.plan.n_stream * keys_stream);
   const int64_t unit = (int64_t)kDecodeKeys * kDecodeWaves;
   int64_t split = (total + kDecodeTargetItems - 1) / kDecodeTargetItems;
@@ -179,22 +188,23 @@ int build_decode(const Layer& L, int32_t batch, int64_t max_seq_len, int64_t mai
   p->n_split_max = p->n_split_main > p->n_split_stream ? p->n_split_main : p->n_split_stream;
   const int64_t im = (int64_t)batch * L.plan.n_main * p->n_split_main;
   const int64_t is = (int64_t)batch * L.plan.n_stream * p->n_split_stream;
-  if (im + is > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "decode work too large for one launch");
+  if ((im + is) * p->n_cb > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "decode work too large for one launch");
   p->n_items_main = (int32_t)im;
   p->n_items = (int32_t)(im + is);
   return DUO_OK;
 }
 
-// Workspace: [B * Hkv] int32 arrival counters | [B, Hq, splits, 2] partial
-// (max, sum) | [B, Hq, splits, 128] partial outputs; each part 256-byte aligned.
+// Workspace: [B * Hkv * column blocks] int32 arrival counters |
+// [B, T, Hq, splits, 2] partial (max, sum) | [B, T, Hq, splits, 128] partial
+// outputs; each part 256-byte aligned.
 struct WsLayout { size_t count, ml, acc, total; };
 
 WsLayout decode_ws_layout(const DecodeParams& p) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  const size_t n = (size_t)p.batch * p.hq * (size_t)p.n_split_max;
+  const size_t n = (size_t)p.batch * p.T * p.hq * (size_t)p.n_split_max;
   WsLayout w;
   w.count = 0;
-  w.ml = up((size_t)p.batch * p.hkv * sizeof(int32_t));
+  w.ml = up((size_t)p.batch * p.hkv * p.n_cb * sizeof(int32_t));
   w.acc = w.ml + up(n * 2 * sizeof(float));
   w.total = w.acc + n * kD * sizeof(float);
   return w;
@@ -440,6 +450,67 @@ int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t b
   p.ws_ml = reinterpret_cast<float*>(ws + wl.ml);
   p.ws_acc = reinterpret_cast<float*>(ws + wl.acc);
   return hip_status(launch_decode(p, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+size_t duo_attn_decode_block_workspace_bytes(const duo_layer* layer, int32_t batch, int32_t num_tokens,
+                                             int64_t max_past_len) {
+  Layer L;
+  if (check_layer(layer, &L)) return 0;
+  if (batch <= 0 || num_tokens < 1 || num_tokens > kMaxBlockTokens || max_past_len < 0 ||
+      max_past_len + num_tokens > kMaxPos)
+    return 0;
+  DecodeParams p;
+  if (build_decode(L, batch, max_past_len, L.main_ring ? L.window : (max_past_len > 0 ? max_past_len : 1), &p,
+                   num_tokens))
+    return 0;
+  ok();
+  return decode_ws_bytes(p);
+}
+
+int duo_attn_decode_block(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch, const void* q,
+                          const void* k_new, const void* v_new, int32_t num_tokens, const int32_t* past_lens,
+                          int64_t max_past_len, void* out, float* lse, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  if (batch < 0) return fail(DUO_ERR_INVALID_ARG, "batch must be >= 0");
+  if (num_tokens < 1 || num_tokens > kMaxBlockTokens)
+    return fail(DUO_ERR_INVALID_ARG, "num_tokens must be in [1, %d]", kMaxBlockTokens);
+  if (batch == 0) return ok();
+  if (max_past_len < 0 || max_past_len + num_tokens > kMaxPos) return fail(DUO_ERR_INVALID_ARG, "max_past_len out of range");
+  if (q == nullptr || k_new == nullptr || v_new == nullptr || past_lens == nullptr || out == nullptr)
+    return fail(DUO_ERR_INVALID_ARG, "q, k_new, v_new, past_lens and out must not be NULL");
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(out))
+    return fail(DUO_ERR_INVALID_ARG, "q, k_new, v_new and out must be 16-byte aligned");
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(DUO_ERR_INVALID_ARG, "lse misaligned");
+  if ((rc = check_cache(L, cache, true, true))) return rc;
+  if (L.plan.n_main > 0 && !L.main_ring && max_past_len > cache->main_capacity)
+    return fail(DUO_ERR_CAPACITY, "max_past_len %lld exceeds main_capacity %lld", (long long)max_past_len,
+                (long long)cache->main_capacity);
+  DecodeParams p;
+  const int64_t main_cap = L.main_ring ? L.window : (L.plan.n_main > 0 ? cache->main_capacity : 1);
+  if ((rc = build_decode(L, batch, max_past_len, main_cap, &p, num_tokens))) return rc;
+  const size_t need = decode_ws_bytes(p);
+  if (workspace == nullptr || workspace_bytes < need)
+    return fail(DUO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DUO_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  p.q = static_cast<const uint16_t*>(q);
+  p.k_new = static_cast<const uint16_t*>(k_new);
+  p.v_new = static_cast<const uint16_t*>(v_new);
+  p.seq_lens = past_lens;
+  p.out = static_cast<uint16_t*>(out);
+  p.lse = lse;
+  p.k_main = static_cast<const uint16_t*>(cache->k_main);
+  p.v_main = static_cast<const uint16_t*>(cache->v_main);
+  p.k_stream = static_cast<const uint16_t*>(cache->k_stream);
+  p.v_stream = static_cast<const uint16_t*>(cache->v_stream);
+  const WsLayout wl = decode_ws_layout(p);
+  char* ws = static_cast<char*>(workspace);
+  p.ws_count = reinterpret_cast<int32_t*>(ws + wl.count);
+  p.ws_ml = reinterpret_cast<float*>(ws + wl.ml);
+  p.ws_acc = reinterpret_cast<float*>(ws + wl.acc);
+  return hip_status(launch_decode_block(p, static_cast<hipStream_t>(stream)), "decode block launch");
 }
 
 int duo_attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {

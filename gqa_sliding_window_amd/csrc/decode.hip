@@ -45,6 +45,49 @@ __device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t*
   }
 }
 
+// Block decode: key index k < n_valid is cache slot k, k >= n_valid is row
+// k - n_valid of the block's own K/V (stride `bstride` elements per token).
+__device__ __forceinline__ void load_tile_block(const uint16_t* kbase, const uint16_t* vbase,
+                                                const uint16_t* kblk, const uint16_t* vblk, int64_t bstride,
+                                                int64_t n_valid, int64_t k0, int64_t k_end, int ld_row,
+                                                int ld_chunk, u32x4 (&stK)[8], u32x4 (&stV)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int64_t key = k0 + ld_row + 4 * j;
+    key = key < k_end ? key : k_end - 1;
+    const bool cached = key < n_valid;
+    const uint16_t* kp = cached ? kbase + key * kD : kblk + (key - n_valid) * bstride;
+    const uint16_t* vp = cached ? vbase + key * kD : vblk + (key - n_valid) * bstride;
+    stK[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + ld_chunk * 8));
+    stV[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + ld_chunk * 8));
+  }
+}
+
+// Block decode visibility of key index k for this lane's query (column):
+// position of cache slot k from the slot contract (a ring that has wrapped
+// holds the newest positions below `past`), block key k at past + (k -
+// n_valid); visible when not after the query and inside the class's band
+// (sliding window of the main class, sink + recent of a streaming head).
+struct BlockVis {
+  int n_valid;     // cache slots
+  int past;        // cached positions [0, past)
+  int q_pos;       // this lane's query position
+  int lo;          // lowest visible position of the band (INT32_MIN: none)
+  int sink;        // positions below it are visible regardless of the band
+  int ring_first;  // first ring slot, or -1 when slot = position
+  int ring_len, wraps, rem;
+  __device__ __forceinline__ int pos(int k) const {
+    if (k >= n_valid) return past + (k - n_valid);
+    if (ring_first < 0 || k < ring_first) return k;
+    const int kr = k - ring_first;
+    return ring_first + kr + ring_len * (wraps - (kr > rem ? 1 : 0));
+  }
+  __device__ __forceinline__ bool visible(int k) const {
+    const int ps = pos(k);
+    return ps <= q_pos && (ps < sink || ps >= lo);
+  }
+};
+
 // Registers -> this wave's private LDS tile; the wave barrier orders the
 // previous tile's reads before the overwrite and these writes before the reads.
 __device__ __forceinline__ void stage_tile(uint16_t* sK, uint16_t* sV, int ld_row, int ld_chunk,
@@ -63,9 +106,12 @@ __device__ __forceinline__ void stage_tile(uint16_t* sK, uint16_t* sV, int ld_ro
 
 // One 32-key tile from LDS: S^T = K Q^T, mask slots >= k_end, online softmax
 // update of (m, l, o) for the wave's 16 columns, O^T += V^T P^T.
+// (kBlock: keys are masked per lane by `bv` on tiles where `mask_all` or the
+// tile reaches the block keys or the item end.)
+template <bool kBlock>
 __device__ __forceinline__ void attend_tile(const uint16_t* sK, const uint16_t* sV, const bf16x8 (&qf)[4],
                                             int64_t k0, int64_t k_end, float c, int r16, int g, float& m,
-                                            float& l, f32x4 (&o)[8]) {
+                                            float& l, f32x4 (&o)[8], const BlockVis& bv, bool mask_all) {
   f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int ds = 0; ds < 4; ++ds) {
@@ -75,7 +121,17 @@ __device__ __forceinline__ void attend_tile(const uint16_t* sK, const uint16_t* 
       s[kt] = mfma_16x16x32(a, qf[ds], s[kt]);
     }
   }
-  if (k0 + kDecodeKeys > k_end) {
+  if (kBlock) {
+    if (mask_all || k0 + kDecodeKeys > bv.n_valid || k0 + kDecodeKeys > k_end) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t k = k0 + 16 * kt + 4 * g + i;
+          if (k >= k_end || !bv.visible((int)k)) s[kt][i] = kNegInf;
+        }
+    }
+  } else if (k0 + kDecodeKeys > k_end) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -136,37 +192,52 @@ __device__ __forceinline__ void write_out_pair(const DecodeParams& p, int64_t bh
   *reinterpret_cast<bf16x2*>(p.out + bh * kD + dim) = r;
 }
 
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
+// One work item: (sequence, KV head, split) and, for the block decode, one
+// 16-wide block of its (query token, query head) columns.
+template <bool kBlock>
+__device__ __forceinline__ void decode_body(const DecodeParams& p) {
   // K/V tiles of the 4 waves; reused after the key loop for the combine/merge.
   __shared__ __attribute__((aligned(16))) uint16_t smem[kDecodeWaves * 2 * kTileElems];
   __shared__ float s_ml[kDecodeWaves][16][2];
   __shared__ int s_last;
 
-  const DecodeItem it = decode_item(p, blockIdx.x);
+  const int cb = kBlock ? (int)(blockIdx.x % p.n_cb) : 0;
+  const DecodeItem it = decode_item(p, kBlock ? (int)(blockIdx.x / p.n_cb) : (int)blockIdx.x);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int r16 = lane & 15;
   const int g = lane >> 4;
   const int G = p.group;
+  const int T = kBlock ? p.T : 1;
 
   const int64_t len = p.seq_lens[it.b];
   const int n_valid = (int)decode_valid_slots(p, it.cls, len > 0 ? len : 0);  // < 2^31
+  const int n_keys = n_valid + (kBlock ? T : 0);
   const int n_planned = (it.cls == kStream) ? p.n_split_stream : p.n_split_main;
-  int n_used = (n_valid + p.split_keys - 1) / p.split_keys;
+  int n_used = (n_keys + p.split_keys - 1) / p.split_keys;
   if (n_used > n_planned) n_used = n_planned;  // a length beyond the planned maximum is cut
   const int64_t k_begin = (int64_t)it.split * p.split_keys;
   int64_t k_end = k_begin + p.split_keys;
-  if (k_end > n_valid) k_end = n_valid;
-  const int64_t bh0 = (int64_t)it.b * p.hq + (int64_t)it.kvh * G;  // first query head row
+  if (k_end > n_keys) k_end = n_keys;
+
+  // Columns of this item: (token t, head g) = (c / G, c % G), c in
+  // [col0, col0 + n_cols); output row of column c.
+  const int col0 = 16 * cb;
+  const int n_cols = min(16, T * G - col0);
+  auto row_of = [&](int c) -> int64_t {
+    const int cc = col0 + c;
+    return kBlock ? (((int64_t)it.b * T + cc / G) * p.hq + (int64_t)it.kvh * G + cc % G)
+                  : ((int64_t)it.b * p.hq + (int64_t)it.kvh * G + cc);
+  };
 
   if (it.split >= n_used) {
-    // empty split; split 0 of an empty sequence writes the zero rows
+    // empty split; split 0 of a sequence without keys writes the zero rows
     if (it.split == 0) {
-      for (int e = tid; e < G * (kD / 2); e += 256) {
-        const int h = e / (kD / 2);
-        *reinterpret_cast<uint32_t*>(p.out + (bh0 + h) * kD + 2 * (e % (kD / 2))) = 0u;
-        if (p.lse != nullptr && (e % (kD / 2)) == 0) p.lse[bh0 + h] = kNegInf;
+      for (int e = tid; e < n_cols * (kD / 2); e += 256) {
+        const int64_t row = row_of(e / (kD / 2));
+        *reinterpret_cast<uint32_t*>(p.out + row * kD + 2 * (e % (kD / 2))) = 0u;
+        if (p.lse != nullptr && (e % (kD / 2)) == 0) p.lse[row] = kNegInf;
       }
     }
     return;
@@ -184,16 +255,53 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
     vbase = p.v_main + off;
   }
 
-  // Q fragments: column r16 = query head kvh * G + r16 (zero beyond G).
+  // Q fragments: lane column r16 (zero beyond the item's columns).
   bf16x8 qf[4];
   {
-    const bool ok = r16 < G;
-    const uint16_t* src = p.q + (bh0 + (ok ? r16 : 0)) * kD + 8 * g;
+    const bool ok = r16 < n_cols;
+    const uint16_t* src = p.q + row_of(ok ? r16 : 0) * kD + 8 * g;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
       u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(src + 32 * ds) : u32x4{0u, 0u, 0u, 0u};
       qf[ds] = __builtin_bit_cast(bf16x8, raw);
     }
+  }
+
+  // Block decode: visibility of each key for this lane's query token.
+  BlockVis bv{};
+  bool mask_all = false;
+  const uint16_t* kblk = nullptr;
+  const uint16_t* vblk = nullptr;
+  const int64_t bstride = (int64_t)p.hkv * kD;
+  if (kBlock) {
+    const int past = len > 0 ? (int)len : 0;  // cached positions [0, past)
+    const int t = (r16 < n_cols ? col0 + r16 : col0) / G;
+    bv.n_valid = n_valid;
+    bv.past = past;
+    bv.q_pos = past + t;
+    bv.lo = INT32_MIN;
+    bv.sink = 0;
+    bv.ring_first = -1;
+    int ring_len = 0, first = 0;
+    if (it.cls == kStream) {
+      bv.lo = bv.q_pos - p.recent + 1;
+      bv.sink = p.sink;
+      first = p.sink;
+      ring_len = p.recent;
+    } else if (p.main_ring) {
+      bv.lo = bv.q_pos - p.window + 1;
+      ring_len = (int)p.main_cap;
+    }
+    if (ring_len > 0 && past > first + ring_len) {  // the ring has wrapped
+      const int rel = past - 1 - first;
+      bv.ring_first = first;
+      bv.ring_len = ring_len;
+      bv.wraps = rel / ring_len;
+      bv.rem = rel - bv.wraps * ring_len;
+    }
+    mask_all = ring_len > 0;  // a band: the oldest cached positions can fall out of it
+    kblk = p.k_new + ((int64_t)it.b * T * p.hkv + it.kvh) * kD;
+    vblk = p.v_new + ((int64_t)it.b * T * p.hkv + it.kvh) * kD;
   }
 
   uint16_t* sK = smem + wave * 2 * kTileElems;
@@ -207,33 +315,40 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  auto load = [&](int64_t k0, u32x4 (&bk)[8], u32x4 (&bvv)[8]) {
+    if (kBlock)
+      load_tile_block(kbase, vbase, kblk, vblk, bstride, n_valid, k0, k_end, ld_row, ld_chunk, bk, bvv);
+    else
+      load_tile(kbase, vbase, k0, k_end, ld_row, ld_chunk, bk, bvv);
+  };
+
   // This wave's tiles start at k_begin + 32 * (wave + 4 t). Two tiles are kept
   // in flight (register buffers A and B, used alternately). Loads are issued
   // unconditionally so the wait counts stay exact: a tile past the split end
-  // reads the last valid slot and is fully masked, leaving (m, l, o) unchanged.
+  // reads the last valid key and is fully masked, leaving (m, l, o) unchanged.
   const int64_t stride = (int64_t)kDecodeKeys * kDecodeWaves;
   const int64_t first = k_begin + (int64_t)kDecodeKeys * wave;
   const int64_t nt = first < k_end ? (k_end - first + stride - 1) / stride : 0;
   u32x4 aK[8], aV[8], bK[8], bV[8];
   // (scheduling barriers keep each tile's 16 loads contiguous in issue order,
   // so waiting for one buffer never waits for the other)
-  load_tile(kbase, vbase, first, k_end, ld_row, ld_chunk, aK, aV);
+  load(first, aK, aV);
   __builtin_amdgcn_sched_barrier(0);
-  load_tile(kbase, vbase, first + stride, k_end, ld_row, ld_chunk, bK, bV);
+  load(first + stride, bK, bV);
   __builtin_amdgcn_sched_barrier(0);
   for (int64_t t = 0; t < nt; t += 2) {
     const int64_t k0 = first + t * stride;
     stage_tile(sK, sV, ld_row, ld_chunk, aK, aV);
     __builtin_amdgcn_sched_barrier(0);
-    load_tile(kbase, vbase, k0 + 2 * stride, k_end, ld_row, ld_chunk, aK, aV);
+    load(k0 + 2 * stride, aK, aV);
     __builtin_amdgcn_sched_barrier(0);
-    attend_tile(sK, sV, qf, k0, k_end, c, r16, g, m, l, o);
+    attend_tile<kBlock>(sK, sV, qf, k0, k_end, c, r16, g, m, l, o, bv, mask_all);
     __builtin_amdgcn_sched_barrier(0);
     stage_tile(sK, sV, ld_row, ld_chunk, bK, bV);
     __builtin_amdgcn_sched_barrier(0);
-    load_tile(kbase, vbase, k0 + 3 * stride, k_end, ld_row, ld_chunk, bK, bV);
+    load(k0 + 3 * stride, bK, bV);
     __builtin_amdgcn_sched_barrier(0);
-    attend_tile(sK, sV, qf, k0 + stride, k_end, c, r16, g, m, l, o);
+    attend_tile<kBlock>(sK, sV, qf, k0 + stride, k_end, c, r16, g, m, l, o, bv, mask_all);
     __builtin_amdgcn_sched_barrier(0);
   }
   l += __shfl_xor(l, 16);
@@ -251,9 +366,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  // thread -> (column, dim pair) of the G valid columns; 64 threads per column
+  // thread -> (column, dim pair) of the item's columns; 64 threads per column
   const bool single = (n_used == 1);
-  for (int e = tid; e < G * (kD / 2); e += 256) {
+  for (int e = tid; e < n_cols * (kD / 2); e += 256) {
     const int col = e / (kD / 2);
     const int dim = 2 * (e % (kD / 2));
     float M = kNegInf;
@@ -268,12 +383,12 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
       a0 += sc * comb[(w * 16 + col) * kD + dim];
       a1 += sc * comb[(w * 16 + col) * kD + dim + 1];
     }
-    const int64_t bh = bh0 + col;
+    const int64_t row = row_of(col);
     if (single) {
-      write_out_pair(p, bh, dim, a0, a1, 1.f / L);
-      if (p.lse != nullptr && dim == 0) p.lse[bh] = (M + __log2f(L)) * kLn2;
+      write_out_pair(p, row, dim, a0, a1, 1.f / L);
+      if (p.lse != nullptr && dim == 0) p.lse[row] = (M + __log2f(L)) * kLn2;
     } else {
-      const int64_t slot = bh * p.n_split_max + it.split;
+      const int64_t slot = row * p.n_split_max + it.split;
       coherent_store(p.ws_acc + slot * kD + dim, a0);
       coherent_store(p.ws_acc + slot * kD + dim + 1, a1);
       if (dim == 0) {
@@ -290,7 +405,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
   // arrival counter is bumped, so no cache-wide writeback fence is needed.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  int32_t* counter = p.ws_count + (int64_t)it.b * p.hkv + it.kvh;
+  int32_t* counter = p.ws_count + ((int64_t)it.b * p.hkv + it.kvh) * p.n_cb + cb;
   if (tid == 0)
     s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == n_used - 1);
   __syncthreads();
@@ -303,21 +418,22 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
   float* s_w = s_m + 16 * kDecodeMaxSplits;       // [16][kDecodeMaxSplits] weights
   float* s_L = s_w + 16 * kDecodeMaxSplits;       // [16]
   float* red = s_L + 16;                          // [4][16][128]
-  for (int e = tid; e < G * n_used; e += 256) {
+  for (int e = tid; e < n_cols * n_used; e += 256) {
     const int h = e / n_used, sp = e % n_used;
-    const float* ml = p.ws_ml + ((bh0 + h) * p.n_split_max + sp) * 2;
+    const float* ml = p.ws_ml + (row_of(h) * p.n_split_max + sp) * 2;
     s_m[h * kDecodeMaxSplits + sp] = coherent_load(ml);
     s_w[h * kDecodeMaxSplits + sp] = coherent_load(ml + 1);
   }
   __syncthreads();
-  for (int h = wave; h < G; h += kDecodeWaves) {
+  for (int h = wave; h < n_cols; h += kDecodeWaves) {
     float M = kNegInf;
     for (int sp = lane; sp < n_used; sp += 64) M = fmaxf(M, s_m[h * kDecodeMaxSplits + sp]);
 #pragma unroll
     for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
     float L = 0.f;
     for (int sp = lane; sp < n_used; sp += 64) {
-      const float w = fast_exp2(s_m[h * kDecodeMaxSplits + sp] - M);
+      const float ms = s_m[h * kDecodeMaxSplits + sp];
+      const float w = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
       L += w * s_w[h * kDecodeMaxSplits + sp];
       s_w[h * kDecodeMaxSplits + sp] = w;
     }
@@ -325,7 +441,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
     for (int x = 32; x >= 1; x >>= 1) L += __shfl_xor(L, x);
     if (lane == 0) {
       s_L[h] = L;
-      if (p.lse != nullptr) p.lse[bh0 + h] = (M + __log2f(L)) * kLn2;
+      if (p.lse != nullptr) p.lse[row_of(h)] = (M + __log2f(L)) * kLn2;
     }
   }
   __syncthreads();
@@ -340,8 +456,8 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
       const int sp = sp0 + u * kDecodeWaves;
 #pragma unroll
       for (int h = 0; h < kMaxGroup; ++h) {
-        if (h < G && sp < n_used) {
-          const float* src = p.ws_acc + ((bh0 + h) * p.n_split_max + sp) * kD + 2 * lane;
+        if (h < n_cols && sp < n_used) {
+          const float* src = p.ws_acc + (row_of(h) * p.n_split_max + sp) * kD + 2 * lane;
           v[u][h][0] = coherent_load(src);
           v[u][h][1] = coherent_load(src + 1);
         }
@@ -352,7 +468,7 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
       const int sp = sp0 + u * kDecodeWaves;
 #pragma unroll
       for (int h = 0; h < kMaxGroup; ++h) {
-        if (h < G && sp < n_used) {
+        if (h < n_cols && sp < n_used) {
           const float w = s_w[h * kDecodeMaxSplits + sp];
           acc[h][0] += w * v[u][h][0];
           acc[h][1] += w * v[u][h][1];
@@ -362,13 +478,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
   }
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
-    if (h < G) {
+    if (h < n_cols) {
       red[(wave * 16 + h) * kD + 2 * lane] = acc[h][0];
       red[(wave * 16 + h) * kD + 2 * lane + 1] = acc[h][1];
     }
   }
   __syncthreads();
-  for (int e = tid; e < G * (kD / 2); e += 256) {
+  for (int e = tid; e < n_cols * (kD / 2); e += 256) {
     const int col = e / (kD / 2);
     const int dim = 2 * (e % (kD / 2));
     float a0 = 0.f, a1 = 0.f;
@@ -377,10 +493,13 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) {
       a0 += red[(w * 16 + col) * kD + dim];
       a1 += red[(w * 16 + col) * kD + dim + 1];
     }
-    write_out_pair(p, bh0 + col, dim, a0, a1, 1.f / s_L[col]);
+    write_out_pair(p, row_of(col), dim, a0, a1, 1.f / s_L[col]);
   }
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
 }
+
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) { decode_body<false>(p); }
+__global__ __launch_bounds__(256, 2) void decode_block_kernel(DecodeParams p) { decode_body<true>(p); }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -389,6 +508,12 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* p, int64_t n) {
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
   if (p.n_items > 0) hipLaunchKernelGGL(decode_kernel, dim3((unsigned)p.n_items), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_block(const DecodeParams& p, hipStream_t s) {
+  if (p.n_items > 0)
+    hipLaunchKernelGGL(decode_block_kernel, dim3((unsigned)((int64_t)p.n_items * p.n_cb)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 

@@ -186,23 +186,29 @@ __host__ __device__ inline int64_t tiles_of(const KeyRange& r) {
 
 // ---------------------------------------------------------------- decode
 struct DecodeParams {
-  const uint16_t* q;     // [B, Hq, D]
-  const int32_t* seq_lens;
-  uint16_t* out;         // [B, Hq, D]
-  float* lse;            // [B, Hq] or null
+  const uint16_t* q;     // [B, T, Hq, D]
+  const int32_t* seq_lens;  // single-token decode: lengths including the query token (its K/V
+                            // already appended); block decode: cached lengths before the block
+  uint16_t* out;         // [B, T, Hq, D]
+  float* lse;            // [B, T, Hq] or null
   const uint16_t* k_main;
   const uint16_t* v_main;
   const uint16_t* k_stream;
   const uint16_t* v_stream;
-  int32_t* ws_count;     // [B, Hkv] arrival counters, zero between calls
-  float* ws_ml;          // [B, Hq, n_split_max, 2] partial (max, sum)
-  float* ws_acc;         // [B, Hq, n_split_max, D] partial unnormalised outputs
+  const uint16_t* k_new; // block decode: the block's own K/V [B, T, Hkv, D]; null otherwise
+  const uint16_t* v_new;
+  int32_t* ws_count;     // [B, Hkv, n_cb] arrival counters, zero between calls
+  float* ws_ml;          // [B, T, Hq, n_split_max, 2] partial (max, sum)
+  float* ws_acc;         // [B, T, Hq, n_split_max, D] partial unnormalised outputs
   int64_t main_cap;      // slots per (b, main head)
   int32_t main_ring;     // main cache is a ring (sliding layer)
+  int32_t window;        // sliding layer window (main class), 0 = none
   int32_t batch, hq, hkv, group;
   int32_t sink, recent;
   int32_t n_main, n_stream;
   uint32_t stream_mask;
+  int32_t T;             // query tokens per sequence (1 for the single-token decode)
+  int32_t n_cb;          // 16-wide MFMA column blocks per work item: ceil(T * G / 16)
   int32_t split_keys;
   int32_t n_split_main, n_split_stream, n_split_max;
   int32_t n_items_main, n_items;
@@ -237,10 +243,17 @@ __host__ __device__ inline int64_t decode_valid_slots(const DecodeParams& p, int
   return len < cap ? len : cap;
 }
 
+// Keys a work item of a (sequence, head) reads: the valid cache slots, then
+// (block decode) the block's own T keys, which follow them in this order.
+__host__ __device__ inline int64_t decode_keys(const DecodeParams& p, int cls, int64_t len, bool block) {
+  return decode_valid_slots(p, cls, len) + (block ? p.T : 0);
+}
+
 // Launchers (defined in the .hip files).
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int64_t n_blocks, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_block(const DecodeParams& p, hipStream_t s);
 hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s);
 
 }  // namespace duo

@@ -159,6 +159,33 @@ int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t b
                     void* out, float* lse, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* Block decode: num_tokens consecutive query tokens per sequence, at
+ * positions past_lens[b] .. past_lens[b] + num_tokens - 1 -- the block a
+ * speculative-decoding target verifies in one pass (SGLang cookbook
+ * "Laguna-XS-2.1", DFlash speculative decoding: the target checks a whole
+ * drafted block at once). Each token sees the visible cached positions
+ * (the same rules as duo_attn_prefill: full-context heads the causal prefix,
+ * a sliding layer its window, streaming heads sink + recent) and the block's
+ * tokens up to itself. Attend, then append: the cache holds positions
+ * [0, past_lens[b]) as duo_kv_append left it, the block's own K/V come from
+ * k_new/v_new; append them afterwards for the next step.
+ * q, out      : device [batch, num_tokens, Hq, 128] bf16.
+ * k_new,v_new : device [batch, num_tokens, Hkv, 128] bf16.
+ * past_lens   : device int32 [batch], each in [0, max_past_len].
+ * max_past_len: host bound; sizes the split-K grid and the workspace.
+ * lse         : NULL or device float [batch, num_tokens, Hq].
+ * num_tokens  : 1 .. 64.
+ * workspace   : as for duo_attn_decode, of duo_attn_decode_block_workspace_bytes()
+ *               bytes (zero-filled once before first use). */
+int duo_attn_decode_block(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch,
+                          const void* q, const void* k_new, const void* v_new, int32_t num_tokens,
+                          const int32_t* past_lens, int64_t max_past_len, void* out, float* lse,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace size for duo_attn_decode_block; 0 on invalid arguments. Host only. */
+size_t duo_attn_decode_block_workspace_bytes(const duo_layer* layer, int32_t batch,
+                                             int32_t num_tokens, int64_t max_past_len);
+
 /* Zero-fill a decode workspace (enqueued on `stream`; a small fill kernel, so
  * it is also safe under graph capture). */
 int duo_attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);

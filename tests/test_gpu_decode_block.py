@@ -1,0 +1,134 @@
+"""duo_attn_decode_block (several query tokens per sequence, attend then
+append) against the float64 oracle.
+
+Each sequence has its own cached length; the cache is filled by
+duo_kv_append with seeded K/V of positions [0, past_b) and the block's own K/V
+are the seeded rows of positions past_b .. past_b + T - 1. The oracle reads
+the same K/V by absolute position and evaluates the block's tokens as prefill
+rows starting at past_b (never from the GPU caches)."""
+import zlib
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from gpu_util import announce, bits_to_f64, check_close, dev, host_bits
+
+pytestmark = pytest.mark.gpu
+
+
+def _kw(layer):
+    return dict(hkv=layer.num_kv_heads, layer="sliding" if layer.kind == 1 else "full",
+                window=layer.window, sink=layer.sink, recent=layer.recent,
+                full_attention_heads=layer.full_attention_heads, scale=layer.scale)
+
+
+def run_block(lib, layer, past, T, seed, cap=None):
+    """Fill the caches to past_b, run the block decode; returns (q, K/V per
+    sequence, out bits [B, T, Hq, D], lse [B, T, Hq])."""
+    import torch
+    B, hq, hkv = len(past), layer.num_q_heads, layer.num_kv_heads
+    ends = [p + T for p in past]
+    k = wl.normal_tokens_ragged(seed, wl.K, [0] * B, ends, hkv, 128)
+    v = wl.normal_tokens_ragged(seed, wl.V, [0] * B, ends, hkv, 128)
+    q = wl.normal_tokens(seed, wl.Q, B, 0, T, hq, 128)
+    cap = cap or max(max(past), 1)
+    cache = lib.KVCache(layer, B, cap)
+    for b in range(B):
+        if past[b] > 0:
+            sp = torch.tensor([0], dtype=torch.int32, device="cuda")
+            lib.kv_append(layer, cache, dev(k[b][None, :past[b]]), dev(v[b][None, :past[b]]), sp,
+                          max_end_pos=past[b], batch=1, batch_offset=b)
+    kn = np.stack([k[b][past[b]:past[b] + T] for b in range(B)])
+    vn = np.stack([v[b][past[b]:past[b] + T] for b in range(B)])
+    out = torch.empty((B, T, hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, T, hq), dtype=torch.float32, device="cuda")
+    ws = lib.decode_block_workspace(layer, B, T, max(past))
+    pl = torch.tensor(past, dtype=torch.int32, device="cuda")
+    lib.attn_decode_block(layer, cache, dev(q), dev(kn), dev(vn), pl, max(past), out, ws, lse=lse)
+    torch.cuda.synchronize()
+    return q, k, v, host_bits(out), lse.cpu().numpy(), (cache, ws, kn, vn, pl, out, lse)
+
+
+def check_block(layer, past, T, q, k, v, out, lse, what):
+    B, hq = len(past), layer.num_q_heads
+    got, ref, lg, lr = [], [], [], []
+    for b in range(B):
+        rows = [(0, h, t) for h in range(hq) for t in range(T)]
+        o_ref, l_ref = oracle.prefill_rows(q[b:b + 1], k[b][None], v[b][None], past[b], rows, **_kw(layer))
+        r = np.asarray(rows)
+        got.append(bits_to_f64(out[b, r[:, 2], r[:, 1]]))
+        lg.append(lse[b, r[:, 2], r[:, 1]].astype(np.float64))
+        ref.append(o_ref)
+        lr.append(l_ref)
+    check_close(np.concatenate(got), np.concatenate(ref), what)
+    err = np.abs(np.concatenate(lg) - np.concatenate(lr)).max()
+    assert err < 1e-3, f"{what}: lse error {err}"
+
+
+CASES = {
+    "full_T4_multisplit": (dict(), [1, 700, 2999, 64], 4),
+    "full_T8_three_column_blocks": (dict(), [0, 130, 1500], 8),
+    "full_T1": (dict(), [5, 1000], 1),
+    "sliding_T4_wrapped": (dict(kind=1, window=512), [100, 511, 512, 513, 2000], 4),
+    "sliding_T8_window_64": (dict(kind=1, window=64), [0, 63, 64, 70, 300], 8),
+    "duo_T4": (dict(full_attention_heads=[0, 1, 0, 0, 1, 0, 0, 0]), [0, 40, 64, 300, 320, 321, 2500], 4),
+    "duo_T8_small_band": (dict(full_attention_heads=[1, 0, 0, 0, 0, 0, 0, 0], sink=4, recent=9),
+                          [0, 3, 4, 12, 13, 14, 40], 8),
+    "all_streaming_T2": (dict(full_attention_heads=[0] * 8), [64, 319, 320, 1000], 2),
+    "group16_T3": (dict(num_q_heads=32, num_kv_heads=2), [77, 1200], 3),
+    "duo_sliding_layer_T5": (dict(kind=1, window=100, full_attention_heads=[1, 0], sink=5, recent=7,
+                                  num_q_heads=4, num_kv_heads=2), [0, 6, 12, 99, 100, 101, 450], 5),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_block_decode_parity(lib, name):
+    kw, past, T = CASES[name]
+    announce(f"decode block {name}")
+    layer = lib.Layer(**kw)
+    seed = zlib.crc32(name.encode()) % 100000
+    q, k, v, out, lse, _ = run_block(lib, layer, past, T, seed)
+    check_block(layer, past, T, q, k, v, out, lse, name)
+
+
+def test_block_of_one_equals_decode_after_append(lib):
+    """T = 1: attending before appending the token equals the single-token
+    decode after appending it."""
+    import torch
+    layer = lib.Layer(full_attention_heads=[0, 1, 0, 0, 1, 0, 0, 0])
+    past = [0, 63, 300, 2000]
+    announce("decode block T=1 vs decode")
+    q, k, v, out, lse, (cache, ws, kn, vn, pl, _, _) = run_block(lib, layer, past, 1, 11, cap=4096)
+    B = len(past)
+    lib.kv_append(layer, cache, dev(kn), dev(vn), pl, max_end_pos=max(past) + 1)
+    o2 = torch.empty((B, layer.num_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    wsd = lib.decode_workspace(layer, B, max(past) + 1)
+    sl = torch.tensor([p + 1 for p in past], dtype=torch.int32, device="cuda")
+    lib.attn_decode(layer, cache, dev(q[:, 0]), sl, max(past) + 1, o2, wsd)
+    torch.cuda.synchronize()
+    a = bits_to_f64(out[:, 0]).reshape(-1)
+    b_ = bits_to_f64(host_bits(o2)).reshape(-1)
+    assert np.abs(a - b_).max() <= 2 ** -7, np.abs(a - b_).max()
+
+
+def test_block_workspace_reuse_and_smaller_call(lib):
+    """A second call on the same workspace (counters left at zero by the
+    first) and a later call with fewer tokens give the oracle's result."""
+    layer = lib.Layer(full_attention_heads=[1, 1, 0, 0, 0, 0, 0, 0])
+    announce("decode block workspace reuse")
+    past, T = [900, 2500, 31], 6
+    q, k, v, out, lse, (cache, ws, kn, vn, pl, o, l) = run_block(lib, layer, past, T, 21)
+    check_block(layer, past, T, q, k, v, out, lse, "reuse call 1")
+    import torch
+    lib.attn_decode_block(layer, cache, dev(q), dev(kn), dev(vn), pl, max(past), o, ws, lse=l)
+    torch.cuda.synchronize()
+    check_block(layer, past, T, q, k, v, host_bits(o), l.cpu().numpy(), "reuse call 2")
+    T2 = 3
+    o3 = torch.empty((len(past), T2, layer.num_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+    l3 = torch.empty((len(past), T2, layer.num_q_heads), dtype=torch.float32, device="cuda")
+    lib.attn_decode_block(layer, cache, dev(q[:, :T2]), dev(kn[:, :T2]), dev(vn[:, :T2]), pl, max(past), o3, ws,
+                          lse=l3)
+    torch.cuda.synchronize()
+    check_block(layer, past, T2, q[:, :T2], k, v, host_bits(o3), l3.cpu().numpy(), "reuse call 3 (T=3)")
