@@ -13,7 +13,8 @@ same way (HIP events on the stream the kernels run on, inputs resident in
 HBM):
   decode      -- KV GB/s of the sliding-window decode (batch 64, window-512
                  ring) and of the DuoAttention decode (batch 16, contexts up to
-                 131072, Bernoulli(0.25) full-head mask); algorithmic bytes =
+                 131072, Bernoulli(0.25) full-head mask), and of block decodes
+                 of 4 and 8 tokens after those contexts; algorithmic bytes =
                  every visible K and V row read once per KV head; several cache
                  replicas are rotated so the 256 MB Infinity Cache cannot serve
                  them;
@@ -157,7 +158,28 @@ def bench_decode_duo(torch, G, wl, timer, warmup, steps, replicas=2):
     nbytes = int(sum(nf * int(x) + ns * min(int(x), sr) for x in L)) * 128 * 2 * 2
     log("decode duo: timing")
     ms = timer.run(lambda i: G.attn_decode(layer, caches[i % replicas], q, sl, w.len_hi, out, ws), warmup, steps)
-    return w, nbytes, ms, replicas, mask, int(L.sum())
+    stats = dict(timer.last)
+    # block decode (verify blocks of T tokens after the same cached contexts):
+    # algorithmic bytes = the visible cached K/V rows (every full-head
+    # position, the whole sink + recent cache of a streaming head) plus the
+    # block's own K/V
+    block = {}
+    gen.manual_seed(w.seed * 7919)
+    for T in (4, 8):
+        qb = torch.randn((w.batch, T, w.hq, 128), generator=gen, device="cuda").to(torch.bfloat16)
+        kb = torch.randn((w.batch, T, w.hkv, 128), generator=gen, device="cuda").to(torch.bfloat16)
+        vb = torch.randn((w.batch, T, w.hkv, 128), generator=gen, device="cuda").to(torch.bfloat16)
+        ob = torch.empty_like(qb)
+        wsb = G.decode_block_workspace(layer, w.batch, T, w.len_hi)
+        nb = nbytes + w.batch * w.hkv * T * 128 * 2 * 2
+        log(f"decode block T={T}: timing")
+        msb = timer.run(lambda i: G.attn_decode_block(layer, caches[i % replicas], qb, kb, vb, sl, w.len_hi, ob, wsb),
+                        warmup, steps)
+        block[f"T{T}"] = {"ms": msb, "kv_bytes": nb, "GB/s": nb / (msb * 1e-3) / 1e9,
+                          "frac_hbm_peak": nb / (msb * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "ms_median": timer.last["median_ms"], "ms_min": timer.last["min_ms"]}
+    timer.last = stats
+    return w, nbytes, ms, replicas, mask, int(L.sum()), block
 
 
 def bench_chunked(torch, G, wl, timer, warmup, steps):
@@ -329,12 +351,13 @@ def main():
                                "frac_hbm_peak": gbs3 / PEAK_HBM_GBS, "cache_replicas": rep3,
                                "ms_median": timer.last["median_ms"], "ms_min": timer.last["min_ms"]}
         log(f"decode sliding: {ms3 * 1e3:.1f} us, {gbs3:.0f} GB/s")
-        w4, nb4, ms4, rep4, mask4, sumL = bench_decode_duo(torch, G, wl, timer, args.warmup, args.steps)
+        w4, nb4, ms4, rep4, mask4, sumL, blk4 = bench_decode_duo(torch, G, wl, timer, args.warmup, args.steps)
         gbs4 = nb4 / (ms4 * 1e-3) / 1e9
         d["duo"] = {"workload": w4.name, "mask": mask4, "sum_context": sumL, "kv_bytes": nb4, "ms": ms4,
                     "GB/s": gbs4, "frac_hbm_peak": gbs4 / PEAK_HBM_GBS, "cache_replicas": rep4,
                     "ms_median": timer.last["median_ms"], "ms_min": timer.last["min_ms"]}
         log(f"decode duo: {ms4 * 1e3:.1f} us, {gbs4:.0f} GB/s")
+        d["duo_block"] = {"workload": w4.name + " (past = the contexts; verify blocks of T tokens)", **blk4}
         res["decode"] = d
 
     if "chunked" in sections:

@@ -188,7 +188,7 @@ int build_decode(const Layer& L, int32_t batch, int64_t max_seq_len, int64_t mai
   p->n_split_max = p->n_split_main > p->n_split_stream ? p->n_split_main : p->n_split_stream;
   const int64_t im = (int64_t)batch * L.plan.n_main * p->n_split_main;
   const int64_t is = (int64_t)batch * L.plan.n_stream * p->n_split_stream;
-  if ((im + is) * p->n_cb > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "decode work too large for one launch");
+  if ((im + is + kXcds) * p->n_cb > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "decode work too large for one launch");
   p->n_items_main = (int32_t)im;
   p->n_items = (int32_t)(im + is);
   return DUO_OK;

@@ -201,8 +201,17 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   __shared__ float s_ml[kDecodeWaves][16][2];
   __shared__ int s_last;
 
-  const int cb = kBlock ? (int)(blockIdx.x % p.n_cb) : 0;
-  const DecodeItem it = decode_item(p, kBlock ? (int)(blockIdx.x / p.n_cb) : (int)blockIdx.x);
+  // Block decode: workgroup i runs on XCD i % 8 (round-robin dispatch); the
+  // n_cb column blocks of one item are consecutive workgroups of the same
+  // XCD, so the second and later readers of its K/V find them in that L2.
+  int cb = 0, item = (int)blockIdx.x;
+  if (kBlock) {
+    const int x = (int)(blockIdx.x % kXcds), j = (int)(blockIdx.x / kXcds);
+    cb = j % p.n_cb;
+    item = (j / p.n_cb) * kXcds + x;
+    if (item >= p.n_items) return;
+  }
+  const DecodeItem it = decode_item(p, item);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -512,8 +521,8 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
 }
 
 hipError_t launch_decode_block(const DecodeParams& p, hipStream_t s) {
-  if (p.n_items > 0)
-    hipLaunchKernelGGL(decode_block_kernel, dim3((unsigned)((int64_t)p.n_items * p.n_cb)), dim3(256), 0, s, p);
+  const int64_t items8 = ((int64_t)p.n_items + kXcds - 1) / kXcds * kXcds;
+  if (p.n_items > 0) hipLaunchKernelGGL(decode_block_kernel, dim3((unsigned)(items8 * p.n_cb)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
