@@ -24,6 +24,6 @@ Readings where the pages are silent are listed in ``oracle.attention``.
 """
 from .attention import (  # noqa: F401
     FULL_LAYER, SLIDING_LAYER, bf16_bits_to_f64, kv_head_of, head_is_streaming,
-    visible_positions, attend, prefill_rows, decode_rows,
+    visible_positions, attend, output_gate, prefill_rows, decode_rows,
 )
 from .cache_model import ShadowCache  # noqa: F401

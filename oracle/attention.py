@@ -33,6 +33,18 @@ R10 window <= 0 means no window (Laguna-M.1-8bit post, implementation
 R11 Default scale is 1/sqrt(D).
 R12 Decode: a sequence of length L has its current token at position L-1
    already in the cache; the query attends positions 0..L-1 by the same rule.
+R17 Block decode (T tokens after past_b cached positions): token t is at
+   position past_b + t and attends by the same rule, so the block's rows are
+   prefill rows starting at past_b.
+R15 Attention sink of a sliding layer (Laguna-M.1-8bit post, section on the
+   sliding-window optimisations: a learnable bias added for sliding-window
+   layers): one logit per query head, in the units of the scaled logits,
+   that enters the softmax normaliser with a zero value row.
+R16 Output gate (same post, attention output gating; the gating options it
+   lists are one gate per (head, channel) or one per head broadcast over the
+   channels): the attention output times the logistic function of the gating
+   projection's value. The logistic form is the plainest reading; the post
+   does not name the nonlinearity.
 """
 from __future__ import annotations
 
@@ -82,20 +94,41 @@ def visible_positions(i: int, layer: str, window: int, streaming: bool,
     return np.arange(0, i + 1, dtype=np.int64)
 
 
-def attend(qvec: np.ndarray, kmat: np.ndarray, vmat: np.ndarray, scale: float):
+def attend(qvec: np.ndarray, kmat: np.ndarray, vmat: np.ndarray, scale: float, sink_logit=None):
     """Softmax attention of one query over the given keys/values (float64).
 
     logits s_j = scale * <q, k_j>; weights w_j = exp(s_j - max s) / sum;
     output sum_j w_j v_j; lse = max s + ln(sum exp(s_j - max s)).
     Returns (output[D], lse). An empty key set returns zeros and -inf.
+
+    sink_logit (reading R15): the learnable bias of a sliding layer's
+    attention sink (Laguna-M.1-8bit blog post, section on the sliding-window
+    optimisations) joins the normaliser as one more logit whose value row is
+    zero: the denominator gains exp(sink_logit) and lse includes it.
     """
-    if kmat.shape[0] == 0:
-        return np.zeros(qvec.shape[0]), -np.inf
-    s = scale * (kmat @ qvec)
-    m = s.max()
+    s = scale * (kmat @ qvec) if kmat.shape[0] else np.zeros(0)
+    if sink_logit is None:
+        if kmat.shape[0] == 0:
+            return np.zeros(qvec.shape[0]), -np.inf
+        m = s.max()
+        w = np.exp(s - m)
+        z = w.sum()
+        return (w @ vmat) / z, m + np.log(z)
+    b = float(sink_logit)
+    m = max(s.max(), b) if len(s) else b
     w = np.exp(s - m)
-    z = w.sum()
-    return (w @ vmat) / z, m + np.log(z)
+    z = w.sum() + np.exp(b - m)
+    out = (w @ vmat) / z if len(s) else np.zeros(qvec.shape[0])
+    return out, m + np.log(z)
+
+
+def output_gate(out: np.ndarray, gate: np.ndarray) -> np.ndarray:
+    """Gated attention output (reading R16): each output channel times the
+    logistic function of its gate value, which comes from the layer's gating
+    projection (Laguna-M.1-8bit blog post, attention output gating: one gate
+    per (head, channel), or one per head broadcast over the head's channels).
+    `gate` broadcasts against `out` ([n, D] or [n, 1])."""
+    return out / (1.0 + np.exp(-np.asarray(gate, dtype=np.float64)))
 
 
 def _rows(vis: np.ndarray):
@@ -112,7 +145,7 @@ def _layer_scale(d: int, scale):
 
 def prefill_rows(q, k_pos, v_pos, start_pos: int, rows, *, hkv: int, layer: str,
                  window: int = 0, sink: int = 64, recent: int = 256,
-                 full_attention_heads=None, scale=None):
+                 full_attention_heads=None, scale=None, sink_logits=None):
     """Reference outputs for selected prefill query rows.
 
     q      : uint16 bf16 bits [B, T, Hq, D] -- queries at positions
@@ -121,6 +154,7 @@ def prefill_rows(q, k_pos, v_pos, start_pos: int, rows, *, hkv: int, layer: str,
              position (N >= start_pos + T); every position a row can see
              must be filled.
     rows   : iterable of (b, h, t) with t the row inside the chunk.
+    sink_logits : None or [Hq] attention-sink logits (see ``attend``).
     Returns (out float64 [n, D], lse float64 [n]).
     """
     rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
@@ -140,12 +174,14 @@ def prefill_rows(q, k_pos, v_pos, start_pos: int, rows, *, hkv: int, layer: str,
             cache[key] = (bf16_bits_to_f64(k_pos[b, :, kvh]), bf16_bits_to_f64(v_pos[b, :, kvh]))
         kf, vf = cache[key]
         sel = _rows(vis)
-        out[n], lse[n] = attend(bf16_bits_to_f64(q[b, t, h]), kf[sel], vf[sel], sc)
+        sl = None if sink_logits is None else sink_logits[int(h)]
+        out[n], lse[n] = attend(bf16_bits_to_f64(q[b, t, h]), kf[sel], vf[sel], sc, sl)
     return out, lse
 
 
 def decode_rows(q, kv_of, lengths, rows, *, hkv: int, layer: str, window: int = 0,
-                sink: int = 64, recent: int = 256, full_attention_heads=None, scale=None):
+                sink: int = 64, recent: int = 256, full_attention_heads=None, scale=None,
+                sink_logits=None):
     """Reference outputs for decode: one query per sequence at position L_b - 1
     (reading R12).
 
@@ -173,5 +209,6 @@ def decode_rows(q, kv_of, lengths, rows, *, hkv: int, layer: str, window: int = 
             kb, vb = kv_of(int(b), kvh, vis)
             cache[key] = (bf16_bits_to_f64(kb), bf16_bits_to_f64(vb))
         kf, vf = cache[key]
-        out[n], lse[n] = attend(bf16_bits_to_f64(q[b, h]), kf, vf, sc)
+        sl = None if sink_logits is None else sink_logits[int(h)]
+        out[n], lse[n] = attend(bf16_bits_to_f64(q[b, h]), kf, vf, sc, sl)
     return out, lse

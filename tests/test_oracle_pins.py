@@ -320,3 +320,61 @@ def test_workloads_use_the_pages_geometry():
     assert workloads.WORKLOADS[1].window == g["window"] and workloads.WORKLOADS[3].window == g["window"]
     assert workloads.WORKLOADS[1].hq // workloads.WORKLOADS[1].hkv == g["num_q_heads"] // g["num_kv_heads"]
     assert g["layers_sliding"] + g["layers_full"] == g["layers_total"]
+
+
+# ------------------------------------------------------ attention sink and gate
+def test_sink_closed_form_zero_keys_one_hot_values():
+    """K = 0 makes every logit 0: each of the n visible keys weighs
+    1 / (n + e^b) and the normaliser is n + e^b (sink logit b, zero value)."""
+    n, D = 37, 128
+    q = np.ones(D)
+    k = np.zeros((n, D))
+    v = np.zeros((n, D))
+    for j in range(n):
+        v[j, j] = 1.0
+    for b in (-3.0, 0.0, 2.5, 30.0):
+        out, lse = oa.attend(q, k, v, 0.125, sink_logit=b)
+        assert np.allclose(out[:n], 1.0 / (n + math.exp(b)), rtol=1e-14, atol=0)
+        assert np.all(out[n:] == 0)
+        assert abs(lse - math.log(n + math.exp(b))) < 1e-12
+
+
+def test_sink_equals_library_softmax_with_an_extra_zero_value_key():
+    """The sink is one more key whose logit is b and whose value is zero:
+    torch's float64 softmax attention over the keys plus such a key gives
+    the same output."""
+    import torch
+    rng = np.random.default_rng(7)
+    D, n, scale, b = 128, 50, 0.09, 1.7
+    q = rng.standard_normal(D)
+    k = rng.standard_normal((n, D))
+    v = rng.standard_normal((n, D))
+    k_sink = q * (b / (scale * (q @ q)))            # scale * <q, k_sink> = b
+    ke = np.vstack([k, k_sink])
+    ve = np.vstack([v, np.zeros(D)])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None, None, None], torch.from_numpy(ke)[None, None],
+        torch.from_numpy(ve)[None, None], scale=scale)[0, 0, 0].numpy()
+    out, lse = oa.attend(q, k, v, scale, sink_logit=b)
+    assert np.abs(out - ref).max() < 1e-12
+    s = scale * (ke @ q)
+    assert abs(lse - (s.max() + math.log(np.exp(s - s.max()).sum()))) < 1e-12
+
+
+def test_sink_far_below_every_logit_is_no_sink_and_empty_set_is_sink_only():
+    rng = np.random.default_rng(8)
+    q, k, v = rng.standard_normal(128), rng.standard_normal((20, 128)), rng.standard_normal((20, 128))
+    o1, l1 = oa.attend(q, k, v, 0.1)
+    o2, l2 = oa.attend(q, k, v, 0.1, sink_logit=-800.0)
+    assert np.abs(o1 - o2).max() < 1e-15 and abs(l1 - l2) < 1e-15
+    o3, l3 = oa.attend(q, k[:0], v[:0], 0.1, sink_logit=0.3)
+    assert np.all(o3 == 0) and l3 == 0.3
+
+
+def test_output_gate_values():
+    o = np.linspace(-2, 2, 128)[None]
+    assert np.array_equal(oa.output_gate(o, np.zeros_like(o)), o / 2)       # logistic(0) = 1/2
+    assert np.abs(oa.output_gate(o, np.full_like(o, 60.0)) - o).max() < 1e-25
+    g = np.array([[0.7]])
+    assert np.array_equal(oa.output_gate(o, g), oa.output_gate(o, np.full_like(o, 0.7)))  # per head = broadcast
+    assert abs(oa.output_gate(np.array([1.0]), np.array([math.log(3.0)]))[0] - 0.75) < 1e-15
