@@ -49,7 +49,7 @@ def test_wrong_scale_is_caught(monkeypatch):
 
 
 def test_dropped_max_subtraction_sign_is_caught(monkeypatch):
-    def bad_attend(q, k, v, scale):
+    def bad_attend(q, k, v, scale, sink_logit=None):
         s = scale * (k @ q)
         m = s.max()
         w = np.exp(s + m)          # wrong sign: cancels in the output, not in lse
@@ -60,9 +60,25 @@ def test_dropped_max_subtraction_sign_is_caught(monkeypatch):
 
 
 def test_transposed_value_use_is_caught(monkeypatch):
-    def bad_attend(q, k, v, scale):
+    def bad_attend(q, k, v, scale, sink_logit=None):
         s = scale * (k @ q)
         w = np.exp(s - s.max())
         return (w @ k) / w.sum(), s.max() + np.log(w.sum())   # keys used as values
     monkeypatch.setattr(oa, "attend", bad_attend)
     assert _fails(lambda: pins.test_oracle_matches_torch_sdpa("sliding"))
+
+
+def test_sink_left_out_of_the_normaliser_is_caught(monkeypatch):
+    orig = oa.attend
+
+    def bad_attend(q, k, v, scale, sink_logit=None):
+        out, lse = orig(q, k, v, scale)          # the sink logit is ignored
+        return out, lse
+    monkeypatch.setattr(oa, "attend", bad_attend)
+    assert _fails(pins.test_sink_closed_form_zero_keys_one_hot_values)
+    assert _fails(pins.test_sink_equals_library_softmax_with_an_extra_zero_value_key)
+
+
+def test_gate_with_the_wrong_sign_is_caught(monkeypatch):
+    monkeypatch.setattr(oa, "output_gate", lambda out, gate: out / (1.0 + np.exp(np.asarray(gate, float))))
+    assert _fails(pins.test_output_gate_values)
