@@ -44,6 +44,12 @@ class _Cache(ctypes.Structure):
                 ("k_stream", ctypes.c_void_p), ("v_stream", ctypes.c_void_p)]
 
 
+class _Epilogue(ctypes.Structure):
+    _fields_ = [("sink_logits", ctypes.c_void_p), ("gate", ctypes.c_void_p), ("gate_mode", ctypes.c_int32)]
+
+
+GATE_NONE, GATE_PER_ELEMENT, GATE_PER_HEAD = 0, 1, 2
+
 _lib = None
 
 
@@ -57,14 +63,14 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     P = ctypes.c_void_p
     i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
-    LP, CP = ctypes.POINTER(_Layer), ctypes.POINTER(_Cache)
+    LP, CP, EP = ctypes.POINTER(_Layer), ctypes.POINTER(_Cache), ctypes.POINTER(_Epilogue)
     I32P, I64P = ctypes.POINTER(i32), ctypes.POINTER(i64)
     sigs = {
         "duo_kv_append": (ctypes.c_int, [LP, CP, i32, P, P, i32, P, i64, P]),
-        "duo_attn_prefill": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, i64, P, P, P]),
-        "duo_attn_decode": (ctypes.c_int, [LP, CP, i32, P, P, i64, P, P, P, sz, P]),
+        "duo_attn_prefill": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, i64, P, P, EP, P]),
+        "duo_attn_decode": (ctypes.c_int, [LP, CP, i32, P, P, i64, P, P, P, sz, EP, P]),
         "duo_attn_decode_workspace_bytes": (sz, [LP, i32, i64]),
-        "duo_attn_decode_block": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, P, i64, P, P, P, sz, P]),
+        "duo_attn_decode_block": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, P, i64, P, P, P, sz, EP, P]),
         "duo_attn_decode_block_workspace_bytes": (sz, [LP, i32, i32, i64]),
         "duo_attn_decode_workspace_init": (ctypes.c_int, [P, sz, P]),
         "duo_kv_cache_bytes": (ctypes.c_int, [LP, i32, i64, I64P, I64P]),
@@ -176,16 +182,35 @@ def kv_append(layer: Layer, cache: KVCache, k_new, v_new, start_pos, max_end_pos
                              _ptr(start_pos), int(max_end_pos), _stream(stream)))
 
 
+def _epilogue(out, sink_logits, gate):
+    """duo_epilogue for the call, or None. sink_logits: float32 [Hq];
+    gate: bf16 shaped like `out` (one value per element) or like `out`
+    without its last dimension (one value per row and head)."""
+    if sink_logits is None and gate is None:
+        return None
+    mode = GATE_NONE
+    if gate is not None:
+        if tuple(gate.shape) == tuple(out.shape):
+            mode = GATE_PER_ELEMENT
+        elif tuple(gate.shape) == tuple(out.shape[:-1]):
+            mode = GATE_PER_HEAD
+        else:
+            raise ValueError(f"gate shape {tuple(gate.shape)} matches neither {tuple(out.shape)} "
+                             f"nor {tuple(out.shape[:-1])}")
+    return ctypes.byref(_Epilogue(_ptr(sink_logits), _ptr(gate), mode))
+
+
 def attn_prefill(layer: Layer, q, k, v, out, start_pos: int = 0, past: Optional[KVCache] = None,
-                 lse=None, stream=None):
-    """duo_attn_prefill: q [B, T, Hq, 128], k/v [B, T, Hkv, 128], out like q."""
+                 lse=None, stream=None, sink_logits=None, gate=None):
+    """duo_attn_prefill: q [B, T, Hq, 128], k/v [B, T, Hkv, 128], out like q;
+    optional attention-sink logits and output gate (see _epilogue)."""
     lib = load()
     B, T = q.shape[0], q.shape[1]
     cl = layer._c()
     cc = past._c() if past is not None else None
     _check(lib.duo_attn_prefill(ctypes.byref(cl), ctypes.byref(cc) if cc is not None else None, B,
                                 _ptr(q), _ptr(k), _ptr(v), T, int(start_pos), _ptr(out), _ptr(lse),
-                                _stream(stream)))
+                                _epilogue(out, sink_logits, gate), _stream(stream)))
 
 
 def decode_workspace_bytes(layer: Layer, batch: int, max_seq_len: int) -> int:
@@ -209,7 +234,7 @@ def init_decode_workspace(ws, stream=None):
 
 
 def attn_decode(layer: Layer, cache: KVCache, q, seq_lens, max_seq_len: int, out, workspace,
-                lse=None, stream=None):
+                lse=None, stream=None, sink_logits=None, gate=None):
     """duo_attn_decode: q [B, Hq, 128], seq_lens int32 [B] (device), out like q."""
     lib = load()
     B = q.shape[0]
@@ -217,7 +242,7 @@ def attn_decode(layer: Layer, cache: KVCache, q, seq_lens, max_seq_len: int, out
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib.duo_attn_decode(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(q), _ptr(seq_lens),
                                int(max_seq_len), _ptr(out), _ptr(lse), _ptr(workspace), nbytes,
-                               _stream(stream)))
+                               _epilogue(out, sink_logits, gate), _stream(stream)))
 
 
 def decode_block_workspace_bytes(layer: Layer, batch: int, num_tokens: int, max_past_len: int) -> int:
@@ -236,7 +261,7 @@ def decode_block_workspace(layer: Layer, batch: int, num_tokens: int, max_past_l
 
 
 def attn_decode_block(layer: Layer, cache: KVCache, q, k_new, v_new, past_lens, max_past_len: int, out,
-                      workspace, lse=None, stream=None):
+                      workspace, lse=None, stream=None, sink_logits=None, gate=None):
     """duo_attn_decode_block: q/out [B, T, Hq, 128], k_new/v_new [B, T, Hkv, 128],
     past_lens int32 [B] (device): cached positions before the block."""
     lib = load()
@@ -245,7 +270,8 @@ def attn_decode_block(layer: Layer, cache: KVCache, q, k_new, v_new, past_lens, 
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib.duo_attn_decode_block(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(q), _ptr(k_new), _ptr(v_new),
                                      T, _ptr(past_lens), int(max_past_len), _ptr(out), _ptr(lse),
-                                     _ptr(workspace), nbytes, _stream(stream)))
+                                     _ptr(workspace), nbytes, _epilogue(out, sink_logits, gate),
+                                     _stream(stream)))
 
 
 def head_plan(layer: Layer):

@@ -112,6 +112,26 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Optional epilogue: checks its fields and copies them into the kernel
+// parameters (null epilogue = no sink, no gate).
+int read_epilogue(const duo_epilogue* e, const float** sink, const uint16_t** gate, int32_t* mode) {
+  *sink = nullptr;
+  *gate = nullptr;
+  *mode = DUO_GATE_NONE;
+  if (e == nullptr) return DUO_OK;
+  if (e->sink_logits != nullptr && (reinterpret_cast<uintptr_t>(e->sink_logits) & 3u))
+    return fail(DUO_ERR_INVALID_ARG, "sink_logits misaligned");
+  if (e->gate_mode != DUO_GATE_NONE && e->gate_mode != DUO_GATE_PER_ELEMENT && e->gate_mode != DUO_GATE_PER_HEAD)
+    return fail(DUO_ERR_INVALID_ARG, "unknown gate_mode %d", e->gate_mode);
+  if ((e->gate != nullptr) != (e->gate_mode != DUO_GATE_NONE))
+    return fail(DUO_ERR_INVALID_ARG, "gate and gate_mode must be given together");
+  if (e->gate != nullptr && !aligned16(e->gate)) return fail(DUO_ERR_INVALID_ARG, "gate must be 16-byte aligned");
+  *sink = e->sink_logits;
+  *gate = static_cast<const uint16_t*>(e->gate);
+  *mode = e->gate_mode;
+  return DUO_OK;
+}
+
 // ---- prefill plan
 int build_prefill(const Layer& L, int32_t batch, int32_t T, int64_t start_pos, PrefillParams* p,
                   int64_t* n_blocks) {
@@ -345,7 +365,7 @@ int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens, 
 
 int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t batch, const void* q,
                      const void* k, const void* v, int32_t num_tokens, int64_t start_pos, void* out,
-                     float* lse, void* stream) {
+                     float* lse, const duo_epilogue* epilogue, void* stream) {
   Layer L;
   int rc = check_layer(layer, &L);
   if (rc) return rc;
@@ -370,6 +390,7 @@ int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t b
   PrefillParams p;
   int64_t nb = 0;
   if ((rc = build_prefill(L, batch, num_tokens, start_pos, &p, &nb))) return rc;
+  if ((rc = read_epilogue(epilogue, &p.sink_logits, &p.gate, &p.gate_mode))) return rc;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
@@ -415,7 +436,7 @@ int duo_decode_plan(const duo_layer* layer, int32_t batch, int64_t max_seq_len, 
 
 int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch, const void* q,
                     const int32_t* seq_lens, int64_t max_seq_len, void* out, float* lse, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+                    size_t workspace_bytes, const duo_epilogue* epilogue, void* stream) {
   Layer L;
   int rc = check_layer(layer, &L);
   if (rc) return rc;
@@ -436,6 +457,7 @@ int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t b
   if (workspace == nullptr || workspace_bytes < need)
     return fail(DUO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DUO_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if ((rc = read_epilogue(epilogue, &p.sink_logits, &p.gate, &p.gate_mode))) return rc;
   p.q = static_cast<const uint16_t*>(q);
   p.seq_lens = seq_lens;
   p.out = static_cast<uint16_t*>(out);
@@ -470,7 +492,7 @@ size_t duo_attn_decode_block_workspace_bytes(const duo_layer* layer, int32_t bat
 int duo_attn_decode_block(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch, const void* q,
                           const void* k_new, const void* v_new, int32_t num_tokens, const int32_t* past_lens,
                           int64_t max_past_len, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+                          const duo_epilogue* epilogue, void* stream) {
   Layer L;
   int rc = check_layer(layer, &L);
   if (rc) return rc;
@@ -495,6 +517,7 @@ int duo_attn_decode_block(const duo_layer* layer, const duo_kv_cache* cache, int
   if (workspace == nullptr || workspace_bytes < need)
     return fail(DUO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DUO_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if ((rc = read_epilogue(epilogue, &p.sink_logits, &p.gate, &p.gate_mode))) return rc;
   p.q = static_cast<const uint16_t*>(q);
   p.k_new = static_cast<const uint16_t*>(k_new);
   p.v_new = static_cast<const uint16_t*>(v_new);

@@ -184,11 +184,25 @@ __device__ __forceinline__ float coherent_load(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Output values (dim, dim + 1) of row bh: the unnormalised pair times the
+// row's normaliser and, if the call has one, the output gate.
 __device__ __forceinline__ void write_out_pair(const DecodeParams& p, int64_t bh, int dim, float a0, float a1,
                                                float inv) {
   typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 r = __builtin_convertvector((f32x2{a0 * inv, a1 * inv}), bf16x2);
+  float f0 = inv, f1 = inv;
+  if (p.gate != nullptr) {
+    if (p.gate_mode == 2) {
+      const float gf = gate_factor(bf16_bits_to_f32(p.gate[bh]));
+      f0 *= gf;
+      f1 *= gf;
+    } else {
+      const uint32_t gw = *reinterpret_cast<const uint32_t*>(p.gate + bh * kD + dim);
+      f0 *= gate_factor(bf16_bits_to_f32(gw & 0xffffu));
+      f1 *= gate_factor(bf16_bits_to_f32(gw >> 16));
+    }
+  }
+  const bf16x2 r = __builtin_convertvector((f32x2{a0 * f0, a1 * f1}), bf16x2);
   *reinterpret_cast<bf16x2*>(p.out + bh * kD + dim) = r;
 }
 
@@ -239,6 +253,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     return kBlock ? (((int64_t)it.b * T + cc / G) * p.hq + (int64_t)it.kvh * G + cc % G)
                   : ((int64_t)it.b * p.hq + (int64_t)it.kvh * G + cc);
   };
+  auto head_of = [&](int c) -> int { return it.kvh * G + (kBlock ? (col0 + c) % G : col0 + c); };
 
   if (it.split >= n_used) {
     // empty split; split 0 of a sequence without keys writes the zero rows
@@ -246,7 +261,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       for (int e = tid; e < n_cols * (kD / 2); e += 256) {
         const int64_t row = row_of(e / (kD / 2));
         *reinterpret_cast<uint32_t*>(p.out + row * kD + 2 * (e % (kD / 2))) = 0u;
-        if (p.lse != nullptr && (e % (kD / 2)) == 0) p.lse[row] = kNegInf;
+        if (p.lse != nullptr && (e % (kD / 2)) == 0)  // the sink alone, if any, forms the normaliser
+          p.lse[row] = p.sink_logits != nullptr ? p.sink_logits[head_of(e / (kD / 2))] : kNegInf;
       }
     }
     return;
@@ -394,8 +410,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     }
     const int64_t row = row_of(col);
     if (single) {
-      write_out_pair(p, row, dim, a0, a1, 1.f / L);
-      if (p.lse != nullptr && dim == 0) p.lse[row] = (M + __log2f(L)) * kLn2;
+      const RowNorm rn = row_norm(M, L, p.sink_logits, head_of(col));
+      write_out_pair(p, row, dim, a0, a1, rn.inv);
+      if (p.lse != nullptr && dim == 0) p.lse[row] = rn.lse;
     } else {
       const int64_t slot = row * p.n_split_max + it.split;
       coherent_store(p.ws_acc + slot * kD + dim, a0);
@@ -425,7 +442,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   // partial outputs (wave w takes splits w, w+4, ...; 4 splits per batch).
   float* s_m = reinterpret_cast<float*>(smem);  // [16][kDecodeMaxSplits]
   float* s_w = s_m + 16 * kDecodeMaxSplits;       // [16][kDecodeMaxSplits] weights
-  float* s_L = s_w + 16 * kDecodeMaxSplits;       // [16]
+  float* s_L = s_w + 16 * kDecodeMaxSplits;       // [16] output factors (1 / normaliser)
   float* red = s_L + 16;                          // [4][16][128]
   for (int e = tid; e < n_cols * n_used; e += 256) {
     const int h = e / n_used, sp = e % n_used;
@@ -449,8 +466,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 #pragma unroll
     for (int x = 32; x >= 1; x >>= 1) L += __shfl_xor(L, x);
     if (lane == 0) {
-      s_L[h] = L;
-      if (p.lse != nullptr) p.lse[row_of(h)] = (M + __log2f(L)) * kLn2;
+      const RowNorm rn = row_norm(M, L, p.sink_logits, head_of(h));
+      s_L[h] = rn.inv;
+      if (p.lse != nullptr) p.lse[row_of(h)] = rn.lse;
     }
   }
   __syncthreads();
@@ -502,7 +520,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       a0 += red[(w * 16 + col) * kD + dim];
       a1 += red[(w * 16 + col) * kD + dim + 1];
     }
-    write_out_pair(p, row_of(col), dim, a0, a1, 1.f / s_L[col]);
+    write_out_pair(p, row_of(col), dim, a0, a1, s_L[col]);
   }
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
 }

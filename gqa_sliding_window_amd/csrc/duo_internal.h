@@ -114,6 +114,9 @@ struct PrefillParams {
   int32_t n_units_main;  // (q tile, batch, main head) units
   int32_t n_units;       // all units
   float scale_log2;      // scale * log2(e)
+  const float* sink_logits;  // [Hq] attention-sink logits (natural units) or null
+  const uint16_t* gate;      // bf16 output gate or null
+  int32_t gate_mode;         // 1: gate [B, T, Hq, D]; 2: gate [B, T, Hq]
 };
 
 struct PrefillItem {
@@ -213,6 +216,9 @@ struct DecodeParams {
   int32_t n_split_main, n_split_stream, n_split_max;
   int32_t n_items_main, n_items;
   float scale_log2;
+  const float* sink_logits;  // [Hq] attention-sink logits (natural units) or null
+  const uint16_t* gate;      // bf16 output gate or null
+  int32_t gate_mode;         // 1: gate [B, T, Hq, D]; 2: gate [B, T, Hq]
 };
 
 struct DecodeItem { int32_t cls, b, rank, kvh, split; };

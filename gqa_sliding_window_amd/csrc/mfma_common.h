@@ -64,6 +64,29 @@ __device__ __forceinline__ float wave_xor_max(float v, int mask) {
 
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits) { return __uint_as_float(bits << 16); }
+
+// Final normalisation of one output row. M is the row's running maximum in the
+// log2 domain (x = scaled logit * log2 e) and L the sum of 2^(x - M) over its
+// keys. An attention sink (Laguna-M.1-8bit post, sliding-window optimisations:
+// one learnable logit b per query head, natural units) is one more term of the
+// softmax denominator whose value row is zero. Returns the factor on the
+// unnormalised output and lse = ln(sum e^logit [+ e^b]).
+struct RowNorm { float inv, lse; };
+__device__ __forceinline__ RowNorm row_norm(float M, float L, const float* sink_logits, int qhead) {
+  if (sink_logits == nullptr) return RowNorm{1.f / L, (M + __log2f(L)) * kLn2};
+  const float bs = sink_logits[qhead] * kLog2e;
+  const float Mn = fmaxf(M, bs);
+  const float f = (M == kNegInf) ? 0.f : fast_exp2(M - Mn);
+  const float Ln = L * f + fast_exp2(bs - Mn);
+  return RowNorm{f / Ln, (Mn + __log2f(Ln)) * kLn2};
+}
+
+// Output gate (same post, attention output gating): each output value times
+// the logistic function of its gate value.
+__device__ __forceinline__ float gate_factor(float g) { return 1.f / (1.f + __expf(-g)); }
 // Lazy rescaling: the running row maximum is only moved when a new logit
 // exceeds it by more than this many powers of two; until then exponentials may
 // reach 2^8, far inside fp32 and bf16 range. Output and normaliser share the

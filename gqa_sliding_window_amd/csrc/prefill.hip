@@ -404,7 +404,8 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillPa
   }
 
   if (!wave_active) return;
-  // ---- epilogue: O = O^T / l, bf16 round-to-nearest-even; lse = (m + log2 l) ln 2
+  // ---- epilogue: O = O^T / l (with the attention sink, if any, in l), times
+  // the output gate, bf16 round-to-nearest-even; lse = (m + log2 l) ln 2
 #pragma unroll
   for (int t = 0; t < kRT; ++t) {
     float lt = l[t];
@@ -412,18 +413,41 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillPa
     lt += __shfl_xor(lt, 32);
     const int qpos = qw0 + 16 * t + r16;
     if (qpos > qb) continue;
-    const float inv = 1.f / lt;
-    const int64_t row = (int64_t)it.b * p.T + (qpos - P);
-    uint16_t* dst = p.out + (row * p.hq + it.qhead) * kD + 4 * g;
+    float inv = 1.f / lt;
+    const float mu = (m[t] == kNegInf) ? 0.f : m[t];
+    float lse = (mu + __log2f(lt)) * kLn2;
+    if (p.sink_logits != nullptr) {
+      const RowNorm rn = row_norm(m[t], lt, p.sink_logits, it.qhead);
+      inv = rn.inv;
+      lse = rn.lse;
+    }
+    const int64_t orow = ((int64_t)it.b * p.T + (qpos - P)) * p.hq + it.qhead;
+    uint16_t* dst = p.out + orow * kD + 4 * g;
+    if (p.gate == nullptr) {
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const bf16x4 v = pack_bf16x4(o[t][dt] * inv);
-      *reinterpret_cast<bf16x4*>(dst + 16 * dt) = v;
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x4 v = pack_bf16x4(o[t][dt] * inv);
+        *reinterpret_cast<bf16x4*>(dst + 16 * dt) = v;
+      }
+    } else if (p.gate_mode == 2) {
+      const float f = inv * gate_factor(bf16_bits_to_f32(p.gate[orow]));
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const bf16x4 v = pack_bf16x4(o[t][dt] * f);
+        *reinterpret_cast<bf16x4*>(dst + 16 * dt) = v;
+      }
+    } else {
+      const uint16_t* gsrc = p.gate + orow * kD + 4 * g;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        const uint2 gw = *reinterpret_cast<const uint2*>(gsrc + 16 * dt);
+        const f32x4 gf = f32x4{gate_factor(bf16_bits_to_f32(gw.x & 0xffffu)), gate_factor(bf16_bits_to_f32(gw.x >> 16)),
+                               gate_factor(bf16_bits_to_f32(gw.y & 0xffffu)), gate_factor(bf16_bits_to_f32(gw.y >> 16))};
+        const bf16x4 v = pack_bf16x4(o[t][dt] * inv * gf);
+        *reinterpret_cast<bf16x4*>(dst + 16 * dt) = v;
+      }
     }
-    if (p.lse != nullptr && g == 0) {
-      const float mu = (m[t] == kNegInf) ? 0.f : m[t];
-      p.lse[((int64_t)it.b * p.hq + it.qhead) * p.T + (qpos - P)] = (mu + __log2f(lt)) * kLn2;
-    }
+    if (p.lse != nullptr && g == 0) p.lse[((int64_t)it.b * p.hq + it.qhead) * p.T + (qpos - P)] = lse;
   }
 }
 

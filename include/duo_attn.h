@@ -109,6 +109,32 @@ typedef struct duo_kv_cache {
   void* v_stream;
 } duo_kv_cache;
 
+/* Optional output epilogue of the attention calls (pass NULL for none).
+ * sink_logits : device float [Hq] or NULL. Attention sink of a sliding layer
+ *               (Laguna-M.1-8bit post, sliding-window optimisations: a
+ *               learnable bias added for sliding-window layers): one logit per
+ *               query head, in the units of the scaled logits, that joins the
+ *               softmax normaliser as a key whose value row is zero
+ *               (w_j = e^{s_j} / (sum_i e^{s_i} + e^{b_h})); lse includes it.
+ * gate        : device bf16 or NULL. Output gate (same post, attention output
+ *               gating through a g_proj projection): out = attention output x
+ *               logistic(gate). DUO_GATE_PER_ELEMENT: gate laid out like `out`;
+ *               DUO_GATE_PER_HEAD: like `out` without its last dimension (one
+ *               value per row and query head, broadcast over the 128 channels).
+ * The pages do not name the gate's nonlinearity; the logistic function is the
+ * plainest reading. Both are applied where the kernel normalises each output
+ * row, before the bf16 rounding. Alignment: sink_logits 4 bytes, gate 16
+ * bytes (INVALID_ARG otherwise); gate given without a mode, a mode without a
+ * gate or an unknown mode is INVALID_ARG. The library keeps no pointer after
+ * the call is enqueued; the buffers must stay valid until it completes. */
+enum duo_gate_mode { DUO_GATE_NONE = 0, DUO_GATE_PER_ELEMENT = 1, DUO_GATE_PER_HEAD = 2 };
+
+typedef struct duo_epilogue {
+  const float* sink_logits;
+  const void* gate;
+  int32_t gate_mode;
+} duo_epilogue;
+
 /* Write new K/V rows into the cache (the streaming-head cache manager).
  * k_new, v_new : device [batch, num_tokens, Hkv, 128] (token-major, as the
  *                projections emit them); token t of sequence b is position
@@ -134,16 +160,22 @@ int duo_kv_append(const duo_layer* layer, const duo_kv_cache* cache, int32_t bat
  *       not from the cache (attend, then append the chunk).
  * out : device [batch, num_tokens, Hq, 128] bf16 (round to nearest even).
  * lse : NULL or device float [batch, Hq, num_tokens], natural-log
- *       log-sum-exp of the scaled logits of each row. */
+ *       log-sum-exp of the scaled logits of each row.
+ * epilogue : NULL or the attention sink / output gate (duo_epilogue); a
+ *       per-element gate is [batch, num_tokens, Hq, 128], a per-head gate
+ *       [batch, num_tokens, Hq]. */
 int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t batch,
                      const void* q, const void* k, const void* v, int32_t num_tokens,
-                     int64_t start_pos, void* out, float* lse, void* stream);
+                     int64_t start_pos, void* out, float* lse, const duo_epilogue* epilogue,
+                     void* stream);
 
 /* Decode attention: one query token per sequence at position seq_lens[b]-1,
  * whose K/V have already been appended (seq_lens counts them).
  * q         : device [batch, Hq, 128]
  * seq_lens  : device int32 [batch], each in [1, max_seq_len]; a 0 entry
- *             yields a zero output row (lse = -inf).
+ *             yields a zero output row (lse = -inf, or the sink logit when
+ *             the epilogue has one).
+ * epilogue  : NULL or duo_epilogue; gate [batch, Hq, 128] or [batch, Hq].
  * max_seq_len : host bound used to size the split-K grid.
  * out       : device [batch, Hq, 128] bf16.  lse: NULL or device float [batch, Hq].
  * workspace : device scratch of at least duo_attn_decode_workspace_bytes()
@@ -157,7 +189,7 @@ int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t b
 int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch,
                     const void* q, const int32_t* seq_lens, int64_t max_seq_len,
                     void* out, float* lse, void* workspace, size_t workspace_bytes,
-                    void* stream);
+                    const duo_epilogue* epilogue, void* stream);
 
 /* Block decode: num_tokens consecutive query tokens per sequence, at
  * positions past_lens[b] .. past_lens[b] + num_tokens - 1 -- the block a
@@ -176,11 +208,14 @@ int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t b
  * lse         : NULL or device float [batch, num_tokens, Hq].
  * num_tokens  : 1 .. 64.
  * workspace   : as for duo_attn_decode, of duo_attn_decode_block_workspace_bytes()
- *               bytes (zero-filled once before first use). */
+ *               bytes (zero-filled once before first use).
+ * epilogue    : NULL or duo_epilogue; gate [batch, num_tokens, Hq, 128] or
+ *               [batch, num_tokens, Hq]. */
 int duo_attn_decode_block(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch,
                           const void* q, const void* k_new, const void* v_new, int32_t num_tokens,
                           const int32_t* past_lens, int64_t max_past_len, void* out, float* lse,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          void* workspace, size_t workspace_bytes, const duo_epilogue* epilogue,
+                          void* stream);
 
 /* Workspace size for duo_attn_decode_block; 0 on invalid arguments. Host only. */
 size_t duo_attn_decode_block_workspace_bytes(const duo_layer* layer, int32_t batch,

@@ -205,3 +205,33 @@ def test_visible_pairs_closed_forms():
     L = Layer(kind=SLIDING, window=512, num_q_heads=12, num_kv_heads=2)
     assert g.prefill_flops(L, 1, 1024) == 2417491968
     assert g.prefill_flops(Layer(), 4, 8192) == 3298937536512
+
+
+def test_epilogue_validation_errors(lib):
+    """Bad epilogues are refused on the host before any launch."""
+    q = FakeTensor((1, 8, 48, 128))
+    kv = FakeTensor((1, 8, 8, 128))
+    o = FakeTensor((1, 8, 48, 128))
+    # gate shaped neither like out nor like out without its last dimension
+    with pytest.raises(ValueError):
+        g.attn_prefill(Layer(), q, kv, kv, o, gate=FakeTensor((1, 8, 48, 64), 0x800000), stream=0)
+    # misaligned gate / sink logits
+    assert _err(g.attn_prefill, Layer(), q, kv, kv, o, gate=FakeTensor(o.shape, 0x800008), stream=0) == -1
+    assert _err(g.attn_prefill, Layer(), q, kv, kv, o, sink_logits=FakeTensor((48,), 0x700002), stream=0) == -1
+    # gate_mode without a gate, a gate without a mode, an unknown mode
+    for sl, gate, mode in ((0, 0, 1), (0, 0x800000, 0), (0, 0x800000, 3)):
+        e = g._Epilogue(sl, gate, mode)
+        rc = lib.load().duo_attn_prefill(ctypes.byref(Layer()._c()), None, 1, q.data_ptr(), kv.data_ptr(),
+                                         kv.data_ptr(), 8, 0, o.data_ptr(), None, ctypes.byref(e), None)
+        assert rc == -1, (sl, gate, mode)
+        assert "gate" in lib.load().duo_last_error().decode()
+    # decode and block decode check the epilogue too
+    qd, sl_ = FakeTensor((4, 48, 128)), FakeTensor((4,))
+    ws = FakeTensor((g.decode_workspace_bytes(Layer(), 4, 1000) // 4,), 0x600000)
+    assert _err(g.attn_decode, Layer(), FakeCache(cap=1000), qd, sl_, 1000, qd, ws,
+                gate=FakeTensor((4, 48), 0x800004), stream=0) == -1
+    qb = FakeTensor((4, 2, 48, 128))
+    kvb = FakeTensor((4, 2, 8, 128))
+    wsb = FakeTensor((g.decode_block_workspace_bytes(Layer(), 4, 2, 1000) // 4,), 0x600000)
+    assert _err(g.attn_decode_block, Layer(), FakeCache(cap=1000), qb, kvb, kvb, sl_, 1000, qb, wsb,
+                sink_logits=FakeTensor((48,), 0x700001), stream=0) == -1

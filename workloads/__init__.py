@@ -14,7 +14,11 @@ Recipe (stated once, used everywhere):
     regenerated alone and blocks can be generated in parallel threads;
   * float32 -> bfloat16 is round-to-nearest-even on the bit pattern;
   * context lengths are integers uniform in [lo, hi], inclusive at both ends;
-  * the Duo mask is one Bernoulli(p) draw per KV head, never redrawn.
+  * the Duo mask is one Bernoulli(p) draw per KV head, never redrawn;
+  * the output gate's values are N(0, 1) bf16 like Q/K/V (tensor id GATE);
+    attention-sink logits are float32 uniform in [-2, 8] per query head (the
+    pages give no values for either: the range runs from a sink that barely
+    matters to one that outweighs a few thousand keys).
 Every array handed out is ``uint16`` holding bfloat16 bit patterns.
 """
 from __future__ import annotations
@@ -25,8 +29,8 @@ from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
-# tensor ids used to key value blocks
-Q, K, V = 0, 1, 2
+# tensor ids used to key value blocks (GATE: the output-gate values)
+Q, K, V, GATE = 0, 1, 2, 3
 BLOCK_TOKENS = 1024
 
 
@@ -181,3 +185,9 @@ def sample_query_rows(w: Workload, n_tokens: int, count: int, must=(), chunk: in
     while len(rows) < count:
         rows.add((int(g.integers(w.batch)), int(g.integers(w.hq)), int(g.integers(n_tokens))))
     return np.array(sorted(rows), dtype=np.int64).reshape(-1, 3)
+
+
+def sink_logits(seed: int, hq: int) -> np.ndarray:
+    """float32 [hq]: one attention-sink logit per query head."""
+    ss = np.random.SeedSequence(seed, spawn_key=(GATE, 1))
+    return np.random.Generator(np.random.PCG64(ss)).uniform(-2.0, 8.0, size=hq).astype(np.float32)
