@@ -20,10 +20,14 @@ Every function states the passage of the pages it follows:
 * SGLang cookbook "Laguna-XS-2.1", section 1 "Model Introduction" -- 48 Q /
   8 KV heads, window 512.
 
-Readings where the pages are silent are listed in ``oracle.attention``.
+Readings where the pages are silent are listed in ``oracle.attention`` and
+``oracle.prologue`` (RMSNorm and rotary embedding of q and k).
 """
 from .attention import (  # noqa: F401
     FULL_LAYER, SLIDING_LAYER, bf16_bits_to_f64, kv_head_of, head_is_streaming,
     visible_positions, attend, output_gate, prefill_rows, decode_rows,
 )
 from .cache_model import ShadowCache  # noqa: F401
+from .prologue import (  # noqa: F401
+    rms_norm, yarn_correction_index, rope_frequencies, rope_rotate, qk_prologue,
+)

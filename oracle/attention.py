@@ -60,6 +60,13 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+def values_f64(x) -> np.ndarray:
+    """uint16 arrays are bf16 bit patterns (converted exactly); float arrays
+    are values already (for instance the prologue's float64 outputs)."""
+    x = np.asarray(x)
+    return bf16_bits_to_f64(x) if x.dtype == np.uint16 else x.astype(np.float64)
+
+
 def kv_head_of(h: int, hq: int, hkv: int) -> int:
     """Reading R6: contiguous groups of G = hq / hkv query heads."""
     return h // (hq // hkv)
@@ -149,7 +156,7 @@ def prefill_rows(q, k_pos, v_pos, start_pos: int, rows, *, hkv: int, layer: str,
     """Reference outputs for selected prefill query rows.
 
     q      : uint16 bf16 bits [B, T, Hq, D] -- queries at positions
-             start_pos .. start_pos+T-1.
+             start_pos .. start_pos+T-1 (float arrays: values, see values_f64).
     k_pos, v_pos : uint16 bf16 bits [B, N, Hkv, D] indexed by absolute
              position (N >= start_pos + T); every position a row can see
              must be filled.
@@ -171,11 +178,11 @@ def prefill_rows(q, k_pos, v_pos, start_pos: int, rows, *, hkv: int, layer: str,
         key = (int(b), kvh)
         if key not in cache:
             cache.clear()
-            cache[key] = (bf16_bits_to_f64(k_pos[b, :, kvh]), bf16_bits_to_f64(v_pos[b, :, kvh]))
+            cache[key] = (values_f64(k_pos[b, :, kvh]), values_f64(v_pos[b, :, kvh]))
         kf, vf = cache[key]
         sel = _rows(vis)
         sl = None if sink_logits is None else sink_logits[int(h)]
-        out[n], lse[n] = attend(bf16_bits_to_f64(q[b, t, h]), kf[sel], vf[sel], sc, sl)
+        out[n], lse[n] = attend(values_f64(q[b, t, h]), kf[sel], vf[sel], sc, sl)
     return out, lse
 
 
@@ -207,8 +214,8 @@ def decode_rows(q, kv_of, lengths, rows, *, hkv: int, layer: str, window: int = 
         if key not in cache:
             cache.clear()
             kb, vb = kv_of(int(b), kvh, vis)
-            cache[key] = (bf16_bits_to_f64(kb), bf16_bits_to_f64(vb))
+            cache[key] = (values_f64(kb), values_f64(vb))
         kf, vf = cache[key]
         sl = None if sink_logits is None else sink_logits[int(h)]
-        out[n], lse[n] = attend(bf16_bits_to_f64(q[b, h]), kf, vf, sc, sl)
+        out[n], lse[n] = attend(values_f64(q[b, h]), kf, vf, sc, sl)
     return out, lse
