@@ -29,5 +29,5 @@ from .attention import (  # noqa: F401
 )
 from .cache_model import ShadowCache  # noqa: F401
 from .prologue import (  # noqa: F401
-    rms_norm, yarn_correction_index, rope_frequencies, rope_rotate, qk_prologue,
+    rms_norm, yarn_correction_index, rope_frequencies, rope_rotate, qk_prologue, round_bf16,
 )

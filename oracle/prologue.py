@@ -92,6 +92,16 @@ def rope_rotate(x, positions, freqs, attention_factor: float = 1.0) -> np.ndarra
     return np.concatenate([lo * c - hi * s, hi * c + lo * s], axis=-1) * attention_factor
 
 
+def round_bf16(x) -> np.ndarray:
+    """float64 -> nearest bfloat16 value (8 significant bits, ties to even),
+    returned as float64. The attention consumes bf16 q and k (bf16 matrix
+    products with float32 accumulation), so a prologue's float64 output is
+    rounded once before the attention uses it."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                     # x = m 2^e, 0.5 <= |m| < 1
+    return np.ldexp(np.round(np.ldexp(m, 8)), e - 8)
+
+
 def qk_prologue(x_bits, positions, weight=None, eps: float = 1e-6, rope=None) -> np.ndarray:
     """The prologue on one tensor: x_bits uint16 bf16 bits [n, heads, D] (or
     [n, D]) at positions[n]; RMSNorm when ``weight`` is given, then RoPE when

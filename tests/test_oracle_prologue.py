@@ -143,6 +143,21 @@ def test_qk_prologue_composition():
     assert np.allclose(z[:, 0], z[:, 1])
 
 
+def test_round_bf16_matches_the_bit_level_rounding():
+    """On float32 values (no double rounding possible) it equals the
+    generator's round-to-nearest-even on the bit pattern; exact ties go to
+    the even neighbour; bf16 values are fixed points."""
+    x32 = (np.random.default_rng(3).standard_normal(20000) * np.exp(np.linspace(-20, 20, 20000))).astype(np.float32)
+    want = wl.bf16_bits_to_f32(wl.f32_to_bf16_bits(x32)).astype(np.float64)
+    assert np.array_equal(op.round_bf16(x32.astype(np.float64)), want)
+    one = 1.0
+    assert op.round_bf16(one + 2.0 ** -8) == one                    # tie, 1.0 is even
+    assert op.round_bf16(one + 3 * 2.0 ** -8) == one + 2.0 ** -6    # tie, goes up to even
+    assert op.round_bf16(-(one + 2.0 ** -8 + 2.0 ** -30)) == -(one + 2.0 ** -7)
+    assert np.array_equal(op.round_bf16(want), want)
+    assert op.round_bf16(0.0) == 0.0
+
+
 @pytest.mark.parametrize("mistake", ["interleaved_pairs", "reversed_turn", "ramp_reversed", "norm_over_heads",
                                      "sum_not_mean"])
 def test_planted_prologue_mistakes_are_caught(monkeypatch, mistake):
