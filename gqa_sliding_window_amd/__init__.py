@@ -50,6 +50,49 @@ class _Epilogue(ctypes.Structure):
 
 GATE_NONE, GATE_PER_ELEMENT, GATE_PER_HEAD = 0, 1, 2
 
+
+class _Rope(ctypes.Structure):
+    _fields_ = [("theta", ctypes.c_float), ("factor", ctypes.c_float), ("original_max_position", ctypes.c_int32),
+                ("beta_fast", ctypes.c_float), ("beta_slow", ctypes.c_float), ("attention_factor", ctypes.c_float)]
+
+
+class _Prologue(ctypes.Structure):
+    _fields_ = [("norm_weight", ctypes.c_void_p), ("norm_eps", ctypes.c_float), ("rope", ctypes.POINTER(_Rope))]
+
+
+@dataclass
+class Rope:
+    """Rotary settings (duo_rope). The defaults are the YaRN parameters the
+    Laguna-M.1-8bit post prints for full-attention layers; factor <= 1 gives
+    plain RoPE."""
+    theta: float = 500000.0
+    factor: float = 64.0
+    original_max_position: int = 4096
+    beta_fast: float = 64.0
+    beta_slow: float = 1.0
+    attention_factor: float = 1.0
+
+
+@dataclass
+class Prologue:
+    """RMSNorm weight (device float32 [128] or None) and rotary settings
+    (Rope or None) applied to q or k (duo_prologue)."""
+    norm_weight: object = None
+    eps: float = 1e-6
+    rope: Optional[Rope] = None
+
+    def _c(self):
+        r = None
+        if self.rope is not None:
+            self._rope_c = _Rope(self.rope.theta, self.rope.factor, self.rope.original_max_position,
+                                 self.rope.beta_fast, self.rope.beta_slow, self.rope.attention_factor)
+            r = ctypes.pointer(self._rope_c)
+        return _Prologue(_ptr(self.norm_weight), float(self.eps), r)
+
+
+def _prologue(pro: Optional[Prologue]):
+    return None if pro is None else ctypes.byref(pro._c())
+
 _lib = None
 
 
@@ -64,13 +107,16 @@ def load(path: str = LIB_PATH):
     P = ctypes.c_void_p
     i32, i64, sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     LP, CP, EP = ctypes.POINTER(_Layer), ctypes.POINTER(_Cache), ctypes.POINTER(_Epilogue)
+    PP = ctypes.POINTER(_Prologue)
     I32P, I64P = ctypes.POINTER(i32), ctypes.POINTER(i64)
     sigs = {
-        "duo_kv_append": (ctypes.c_int, [LP, CP, i32, P, P, i32, P, i64, P]),
-        "duo_attn_prefill": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, i64, P, P, EP, P]),
-        "duo_attn_decode": (ctypes.c_int, [LP, CP, i32, P, P, i64, P, P, P, sz, EP, P]),
+        "duo_kv_append": (ctypes.c_int, [LP, CP, i32, P, P, i32, P, i64, PP, P]),
+        "duo_attn_prefill": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, i64, P, P, PP, EP, P]),
+        "duo_attn_decode": (ctypes.c_int, [LP, CP, i32, P, P, i64, P, P, P, sz, PP, EP, P]),
+        "duo_qk_prologue": (ctypes.c_int, [PP, i32, i32, i32, P, P, P, P]),
+        "duo_rope_frequencies": (ctypes.c_int, [ctypes.POINTER(_Rope), ctypes.POINTER(ctypes.c_double)]),
         "duo_attn_decode_workspace_bytes": (sz, [LP, i32, i64]),
-        "duo_attn_decode_block": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, P, i64, P, P, P, sz, EP, P]),
+        "duo_attn_decode_block": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, P, i64, P, P, P, sz, PP, EP, P]),
         "duo_attn_decode_block_workspace_bytes": (sz, [LP, i32, i32, i64]),
         "duo_attn_decode_workspace_init": (ctypes.c_int, [P, sz, P]),
         "duo_kv_cache_bytes": (ctypes.c_int, [LP, i32, i64, I64P, I64P]),
@@ -172,14 +218,36 @@ class KVCache:
 
 
 def kv_append(layer: Layer, cache: KVCache, k_new, v_new, start_pos, max_end_pos: int,
-              batch: Optional[int] = None, batch_offset: int = 0, stream=None):
-    """duo_kv_append: k_new/v_new [B, T, Hkv, 128] bf16, start_pos int32 [B] (device)."""
+              batch: Optional[int] = None, batch_offset: int = 0, stream=None,
+              k_prologue: Optional[Prologue] = None):
+    """duo_kv_append: k_new/v_new [B, T, Hkv, 128] bf16, start_pos int32 [B]
+    (device); k_prologue transforms K on its way into the cache."""
     lib = load()
     B = k_new.shape[0] if batch is None else batch
     T = k_new.shape[1]
     cl, cc = layer._c(), cache._c(batch_offset)
     _check(lib.duo_kv_append(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(k_new), _ptr(v_new), T,
-                             _ptr(start_pos), int(max_end_pos), _stream(stream)))
+                             _ptr(start_pos), int(max_end_pos), _prologue(k_prologue), _stream(stream)))
+
+
+def rope_frequencies(rope: Rope):
+    """duo_rope_frequencies: the 64 rotary angular frequencies (host)."""
+    out = (ctypes.c_double * 64)()
+    r = _Rope(rope.theta, rope.factor, rope.original_max_position, rope.beta_fast, rope.beta_slow,
+              rope.attention_factor)
+    _check(load().duo_rope_frequencies(ctypes.byref(r), out))
+    return list(out)
+
+
+def qk_prologue(prologue: Prologue, x, start_pos, y=None, stream=None):
+    """duo_qk_prologue: y = prologue(x) for x [B, T, H, 128] bf16 at
+    positions start_pos[b] + t (start_pos int32 [B], device); in place when
+    y is None. Returns y."""
+    y = x if y is None else y
+    B, T, H = x.shape[0], x.shape[1], x.shape[2]
+    _check(load().duo_qk_prologue(_prologue(prologue), B, T, H, _ptr(x), _ptr(y), _ptr(start_pos),
+                                  _stream(stream)))
+    return y
 
 
 def _epilogue(out, sink_logits, gate):
@@ -201,7 +269,7 @@ def _epilogue(out, sink_logits, gate):
 
 
 def attn_prefill(layer: Layer, q, k, v, out, start_pos: int = 0, past: Optional[KVCache] = None,
-                 lse=None, stream=None, sink_logits=None, gate=None):
+                 lse=None, stream=None, sink_logits=None, gate=None, q_prologue: Optional[Prologue] = None):
     """duo_attn_prefill: q [B, T, Hq, 128], k/v [B, T, Hkv, 128], out like q;
     optional attention-sink logits and output gate (see _epilogue)."""
     lib = load()
@@ -210,7 +278,7 @@ def attn_prefill(layer: Layer, q, k, v, out, start_pos: int = 0, past: Optional[
     cc = past._c() if past is not None else None
     _check(lib.duo_attn_prefill(ctypes.byref(cl), ctypes.byref(cc) if cc is not None else None, B,
                                 _ptr(q), _ptr(k), _ptr(v), T, int(start_pos), _ptr(out), _ptr(lse),
-                                _epilogue(out, sink_logits, gate), _stream(stream)))
+                                _prologue(q_prologue), _epilogue(out, sink_logits, gate), _stream(stream)))
 
 
 def decode_workspace_bytes(layer: Layer, batch: int, max_seq_len: int) -> int:
@@ -234,7 +302,7 @@ def init_decode_workspace(ws, stream=None):
 
 
 def attn_decode(layer: Layer, cache: KVCache, q, seq_lens, max_seq_len: int, out, workspace,
-                lse=None, stream=None, sink_logits=None, gate=None):
+                lse=None, stream=None, sink_logits=None, gate=None, q_prologue: Optional[Prologue] = None):
     """duo_attn_decode: q [B, Hq, 128], seq_lens int32 [B] (device), out like q."""
     lib = load()
     B = q.shape[0]
@@ -242,7 +310,7 @@ def attn_decode(layer: Layer, cache: KVCache, q, seq_lens, max_seq_len: int, out
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib.duo_attn_decode(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(q), _ptr(seq_lens),
                                int(max_seq_len), _ptr(out), _ptr(lse), _ptr(workspace), nbytes,
-                               _epilogue(out, sink_logits, gate), _stream(stream)))
+                               _prologue(q_prologue), _epilogue(out, sink_logits, gate), _stream(stream)))
 
 
 def decode_block_workspace_bytes(layer: Layer, batch: int, num_tokens: int, max_past_len: int) -> int:
@@ -261,7 +329,8 @@ def decode_block_workspace(layer: Layer, batch: int, num_tokens: int, max_past_l
 
 
 def attn_decode_block(layer: Layer, cache: KVCache, q, k_new, v_new, past_lens, max_past_len: int, out,
-                      workspace, lse=None, stream=None, sink_logits=None, gate=None):
+                      workspace, lse=None, stream=None, sink_logits=None, gate=None,
+                      q_prologue: Optional[Prologue] = None):
     """duo_attn_decode_block: q/out [B, T, Hq, 128], k_new/v_new [B, T, Hkv, 128],
     past_lens int32 [B] (device): cached positions before the block."""
     lib = load()
@@ -270,8 +339,8 @@ def attn_decode_block(layer: Layer, cache: KVCache, q, k_new, v_new, past_lens, 
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib.duo_attn_decode_block(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(q), _ptr(k_new), _ptr(v_new),
                                      T, _ptr(past_lens), int(max_past_len), _ptr(out), _ptr(lse),
-                                     _ptr(workspace), nbytes, _epilogue(out, sink_logits, gate),
-                                     _stream(stream)))
+                                     _ptr(workspace), nbytes, _prologue(q_prologue),
+                                     _epilogue(out, sink_logits, gate), _stream(stream)))
 
 
 def head_plan(layer: Layer):

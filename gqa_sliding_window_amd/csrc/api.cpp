@@ -112,6 +112,61 @@ int hip_status(hipError_t e, const char* what) {
   return ok();
 }
 
+// Optional q/k prologue: checks the fields and fills the device-side
+// settings, including the per-pair turn rates f_i / (2 pi) in double
+// precision. f_i = theta^(-2i/128); with YaRN (factor > 1; Peng et al. 2023,
+// section 3.2) f_i is blended with f_i / factor by a linear ramp over the pair
+// index between floor(c(beta_fast)) and ceil(c(beta_slow)), where c(r) solves
+// original_max_position * theta^(-2c/128) = 2 pi r.
+int read_prologue(const duo_prologue* e, QkPrologue* pr, int32_t* on) {
+  std::memset(pr, 0, sizeof(*pr));
+  *on = 0;
+  if (e == nullptr) return DUO_OK;
+  if (!std::isfinite(e->norm_eps) || e->norm_eps < 0.f) return fail(DUO_ERR_INVALID_ARG, "norm_eps must be finite and >= 0");
+  if (e->norm_weight != nullptr && (reinterpret_cast<uintptr_t>(e->norm_weight) & 3u))
+    return fail(DUO_ERR_INVALID_ARG, "norm_weight misaligned");
+  pr->norm_w = e->norm_weight;
+  pr->eps = e->norm_eps;
+  if (e->rope != nullptr) {
+    const duo_rope& r = *e->rope;
+    if (!(r.theta > 1.f) || !std::isfinite(r.theta)) return fail(DUO_ERR_INVALID_ARG, "rope theta must be finite and > 1");
+    if (!(r.attention_factor > 0.f) || !std::isfinite(r.attention_factor))
+      return fail(DUO_ERR_INVALID_ARG, "rope attention_factor must be finite and > 0");
+    if (!(r.factor > 0.f) || !std::isfinite(r.factor)) return fail(DUO_ERR_INVALID_ARG, "rope factor must be finite and > 0");
+    const double theta = r.theta;
+    const double two_pi = 6.283185307179586476925286766559;
+    double low = 0, high = 0;
+    const bool yarn = r.factor > 1.f;
+    if (yarn) {
+      if (r.original_max_position < 1) return fail(DUO_ERR_INVALID_ARG, "original_max_position must be >= 1");
+      if (!(r.beta_slow > 0.f) || !(r.beta_fast > r.beta_slow) || !std::isfinite(r.beta_fast))
+        return fail(DUO_ERR_INVALID_ARG, "YaRN needs beta_fast > beta_slow > 0");
+      auto corr = [&](double turns) {
+        return kD * std::log(r.original_max_position / (two_pi * turns)) / (2.0 * std::log(theta));
+      };
+      low = std::floor(corr(r.beta_fast));
+      high = std::ceil(corr(r.beta_slow));
+      if (low < 0) low = 0;
+      if (high > kD - 1) high = kD - 1;
+      if (high == low) high += 0.001;
+    }
+    for (int i = 0; i < kD / 2; ++i) {
+      const double f = std::pow(theta, -2.0 * i / kD);
+      double fi = f;
+      if (yarn) {
+        double ramp = (i - low) / (high - low);
+        ramp = ramp < 0 ? 0 : (ramp > 1 ? 1 : ramp);
+        fi = f * (1.0 - ramp) + f / r.factor * ramp;
+      }
+      pr->turns[i] = fi / two_pi;
+    }
+    pr->rope = 1;
+    pr->attn_factor = r.attention_factor;
+  }
+  *on = prologue_active(*pr) ? 1 : 0;
+  return DUO_OK;
+}
+
 // Optional epilogue: checks its fields and copies them into the kernel
 // parameters (null epilogue = no sink, no gate).
 int read_epilogue(const duo_epilogue* e, const float** sink, const uint16_t** gate, int32_t* mode) {
@@ -298,7 +353,7 @@ int duo_kv_cache_report(const duo_layer* layer, int32_t batch, int64_t capacity,
 
 int duo_kv_append(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch, const void* k_new,
                   const void* v_new, int32_t num_tokens, const int32_t* start_pos, int64_t max_end_pos,
-                  void* stream) {
+                  const duo_prologue* k_prologue, void* stream) {
   Layer L;
   int rc = check_layer(layer, &L);
   if (rc) return rc;
@@ -315,6 +370,8 @@ int duo_kv_append(const duo_layer* layer, const duo_kv_cache* cache, int32_t bat
                 (long long)cache->main_capacity);
   if ((int64_t)batch * num_tokens * L.hkv / 16 + 1 > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "append too large");
   AppendParams p{};
+  int32_t pro_on = 0;
+  if ((rc = read_prologue(k_prologue, &p.kpro, &pro_on))) return rc;
   p.k_new = static_cast<const uint16_t*>(k_new);
   p.v_new = static_cast<const uint16_t*>(v_new);
   p.start_pos = start_pos;
@@ -365,7 +422,8 @@ int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens, 
 
 int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t batch, const void* q,
                      const void* k, const void* v, int32_t num_tokens, int64_t start_pos, void* out,
-                     float* lse, const duo_epilogue* epilogue, void* stream) {
+                     float* lse, const duo_prologue* q_prologue, const duo_epilogue* epilogue,
+                     void* stream) {
   Layer L;
   int rc = check_layer(layer, &L);
   if (rc) return rc;
@@ -391,6 +449,7 @@ int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t b
   int64_t nb = 0;
   if ((rc = build_prefill(L, batch, num_tokens, start_pos, &p, &nb))) return rc;
   if ((rc = read_epilogue(epilogue, &p.sink_logits, &p.gate, &p.gate_mode))) return rc;
+  if ((rc = read_prologue(q_prologue, &p.qpro, &p.qpro_on))) return rc;
   p.q = static_cast<const uint16_t*>(q);
   p.k = static_cast<const uint16_t*>(k);
   p.v = static_cast<const uint16_t*>(v);
@@ -436,7 +495,8 @@ int duo_decode_plan(const duo_layer* layer, int32_t batch, int64_t max_seq_len, 
 
 int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch, const void* q,
                     const int32_t* seq_lens, int64_t max_seq_len, void* out, float* lse, void* workspace,
-                    size_t workspace_bytes, const duo_epilogue* epilogue, void* stream) {
+                    size_t workspace_bytes, const duo_prologue* q_prologue, const duo_epilogue* epilogue,
+                    void* stream) {
   Layer L;
   int rc = check_layer(layer, &L);
   if (rc) return rc;
@@ -458,6 +518,7 @@ int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t b
     return fail(DUO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DUO_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if ((rc = read_epilogue(epilogue, &p.sink_logits, &p.gate, &p.gate_mode))) return rc;
+  if ((rc = read_prologue(q_prologue, &p.qpro, &p.qpro_on))) return rc;
   p.q = static_cast<const uint16_t*>(q);
   p.seq_lens = seq_lens;
   p.out = static_cast<uint16_t*>(out);
@@ -492,7 +553,7 @@ size_t duo_attn_decode_block_workspace_bytes(const duo_layer* layer, int32_t bat
 int duo_attn_decode_block(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch, const void* q,
                           const void* k_new, const void* v_new, int32_t num_tokens, const int32_t* past_lens,
                           int64_t max_past_len, void* out, float* lse, void* workspace, size_t workspace_bytes,
-                          const duo_epilogue* epilogue, void* stream) {
+                          const duo_prologue* q_prologue, const duo_epilogue* epilogue, void* stream) {
   Layer L;
   int rc = check_layer(layer, &L);
   if (rc) return rc;
@@ -518,6 +579,7 @@ int duo_attn_decode_block(const duo_layer* layer, const duo_kv_cache* cache, int
     return fail(DUO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DUO_ERR_WORKSPACE, "workspace must be 256-byte aligned");
   if ((rc = read_epilogue(epilogue, &p.sink_logits, &p.gate, &p.gate_mode))) return rc;
+  if ((rc = read_prologue(q_prologue, &p.qpro, &p.qpro_on))) return rc;
   p.q = static_cast<const uint16_t*>(q);
   p.k_new = static_cast<const uint16_t*>(k_new);
   p.v_new = static_cast<const uint16_t*>(v_new);
@@ -542,6 +604,39 @@ int duo_attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void
   return hip_status(launch_fill_zero(static_cast<int32_t*>(workspace), (int64_t)(workspace_bytes / 4),
                                      static_cast<hipStream_t>(stream)),
                     "workspace init launch");
+}
+
+int duo_rope_frequencies(const duo_rope* rope, double* freqs) {
+  if (rope == nullptr || freqs == nullptr) return fail(DUO_ERR_INVALID_ARG, "rope and freqs must not be NULL");
+  duo_prologue e{nullptr, 0.f, rope};
+  QkPrologue pr;
+  int32_t on = 0;
+  const int rc = read_prologue(&e, &pr, &on);
+  if (rc) return rc;
+  for (int i = 0; i < kD / 2; ++i) freqs[i] = pr.turns[i] * 6.283185307179586476925286766559;
+  return ok();
+}
+
+int duo_qk_prologue(const duo_prologue* prologue, int32_t batch, int32_t num_tokens, int32_t heads,
+                    const void* x, void* y, const int32_t* start_pos, void* stream) {
+  if (batch < 0 || num_tokens < 0 || heads < 1 || heads > 4096)
+    return fail(DUO_ERR_INVALID_ARG, "batch, num_tokens must be >= 0 and heads in [1, 4096]");
+  if (prologue == nullptr) return fail(DUO_ERR_INVALID_ARG, "prologue is NULL");
+  PrologueParams p{};
+  int32_t on = 0;
+  int rc = read_prologue(prologue, &p.pr, &on);
+  if (rc) return rc;
+  if (batch == 0 || num_tokens == 0) return ok();
+  if (x == nullptr || y == nullptr || start_pos == nullptr) return fail(DUO_ERR_INVALID_ARG, "x, y and start_pos must not be NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(DUO_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+  if ((int64_t)batch * num_tokens * heads / 32 + 1 > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "prologue too large");
+  p.x = static_cast<const uint16_t*>(x);
+  p.y = static_cast<uint16_t*>(y);
+  p.start_pos = start_pos;
+  p.batch = batch;
+  p.T = num_tokens;
+  p.heads = heads;
+  return hip_status(launch_qk_prologue(p, static_cast<hipStream_t>(stream)), "qk prologue launch");
 }
 
 }  // extern "C"

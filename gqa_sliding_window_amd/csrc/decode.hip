@@ -23,6 +23,7 @@
 // (max, rescale, sum) and resets the counter to zero for the next call.
 #include "duo_internal.h"
 #include "mfma_common.h"
+#include "qk_prologue.h"
 
 namespace duo {
 
@@ -290,6 +291,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(src + 32 * ds) : u32x4{0u, 0u, 0u, 0u};
       qf[ds] = __builtin_bit_cast(bf16x8, raw);
     }
+    // RMSNorm + RoPE of q: the single-token query sits at len - 1, block
+    // token t at past + t.
+    if (p.qpro_on) prologue_frag(qf, kBlock ? (int)len + (col0 + r16) / G : (int)len - 1, g, p.qpro);
   }
 
   // Block decode: visibility of each key for this lane's query token.

@@ -74,6 +74,28 @@ __host__ __device__ inline int head_rank(uint32_t stream_mask, int kvh) {
   return __builtin_popcount((s ? stream_mask : ~stream_mask) & below);
 }
 
+// ---------------------------------------------------------------- q/k prologue
+// RMSNorm weight and rotary settings applied to q or k rows as they are
+// loaded (host-computed turn rates: rotary pair i turns turns[i] times per
+// position).
+struct QkPrologue {
+  const float* norm_w;   // [128] RMSNorm weight, null = no RMSNorm
+  float eps;
+  int32_t rope;          // 1: rotary embedding on
+  float attn_factor;     // multiplies cos and sin
+  double turns[kD / 2];
+};
+
+inline bool prologue_active(const QkPrologue& pr) { return pr.norm_w != nullptr || pr.rope != 0; }
+
+struct PrologueParams {  // standalone prologue: y = prologue(x), [B, T, H, 128]
+  const uint16_t* x;
+  uint16_t* y;
+  const int32_t* start_pos;  // [B]
+  int32_t batch, T, heads;
+  QkPrologue pr;
+};
+
 // ---------------------------------------------------------------- kv append
 struct AppendParams {
   const uint16_t* k_new;
@@ -89,6 +111,7 @@ struct AppendParams {
   int32_t sink, recent;
   int32_t n_main, n_stream;
   uint32_t stream_mask;
+  QkPrologue kpro;      // applied to k_new before it is written (inactive: bit copy)
 };
 
 // ---------------------------------------------------------------- prefill
@@ -117,6 +140,8 @@ struct PrefillParams {
   const float* sink_logits;  // [Hq] attention-sink logits (natural units) or null
   const uint16_t* gate;      // bf16 output gate or null
   int32_t gate_mode;         // 1: gate [B, T, Hq, D]; 2: gate [B, T, Hq]
+  int32_t qpro_on;           // apply qpro to the query rows as they are loaded
+  QkPrologue qpro;
 };
 
 struct PrefillItem {
@@ -219,6 +244,8 @@ struct DecodeParams {
   const float* sink_logits;  // [Hq] attention-sink logits (natural units) or null
   const uint16_t* gate;      // bf16 output gate or null
   int32_t gate_mode;         // 1: gate [B, T, Hq, D]; 2: gate [B, T, Hq]
+  int32_t qpro_on;           // apply qpro to the query rows as they are loaded
+  QkPrologue qpro;
 };
 
 struct DecodeItem { int32_t cls, b, rank, kvh, split; };
@@ -257,6 +284,7 @@ __host__ __device__ inline int64_t decode_keys(const DecodeParams& p, int cls, i
 
 // Launchers (defined in the .hip files).
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
+hipError_t launch_qk_prologue(const PrologueParams& p, hipStream_t s);
 hipError_t launch_prefill(const PrefillParams& p, int64_t n_blocks, hipStream_t s);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_block(const DecodeParams& p, hipStream_t s);

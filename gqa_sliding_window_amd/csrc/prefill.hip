@@ -21,6 +21,7 @@
 // is addressed from one base pointer, other tiles row by row.
 #include "duo_internal.h"
 #include "mfma_common.h"
+#include "qk_prologue.h"
 
 namespace duo {
 
@@ -219,6 +220,7 @@ __global__ __launch_bounds__(kThreads, 8 / kWaves) void prefill_kernel(PrefillPa
       u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(src + 32 * ds) : u32x4{0u, 0u, 0u, 0u};
       qf[t][ds] = __builtin_bit_cast(bf16x8, raw);
     }
+    if (p.qpro_on) prologue_frag(qf[t], qpos, g, p.qpro);  // RMSNorm + RoPE of q, once per row
   }
 
   // ---- key ranges of this work item

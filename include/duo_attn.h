@@ -109,6 +109,46 @@ typedef struct duo_kv_cache {
   void* v_stream;
 } duo_kv_cache;
 
+/* Optional input prologue: RMSNorm of each head's 128 channels, then the
+ * rotary position embedding, applied to q (fused into the attention calls'
+ * query loads), to k on its way into the cache (duo_kv_append), or to any
+ * [batch, tokens, heads, 128] tensor (duo_qk_prologue).
+ * Laguna-XS-2.1 blog post, sliding-window optimisations: q and k are
+ * RMS-normalised before the rotary embedding is applied. Laguna-M.1-8bit blog
+ * post, YaRN dynamic RoPE: full-attention layers use rope_theta 500000, YaRN
+ * factor 64, original_max_position_embeddings 4096, beta_fast 64, beta_slow 1,
+ * attention_factor 1, all 128 channels rotated.
+ *
+ * norm_weight : device float [128] or NULL (no RMSNorm): y = x / sqrt(mean(x^2)
+ *               + norm_eps) * norm_weight over one head's channels (the pages
+ *               give neither the axis nor eps; per head is the plainest
+ *               reading, eps is the caller's). 4-byte aligned.
+ * rope        : host duo_rope or NULL (no rotation); read during the call only.
+ * Rotation: channel i pairs with channel i + 64 and the pair turns by
+ * pos * f_i: (x_i cos - x_{i+64} sin, x_{i+64} cos + x_i sin), both times
+ * attention_factor. f_i = theta^(-2i/128); with factor > 1, YaRN (Peng et
+ * al. 2023, section 3.2, NTK-by-parts) blends f_i and f_i / factor with a
+ * ramp over the pair index between floor(c(beta_fast)) and
+ * ceil(c(beta_slow)), c(r) being the pair index that turns r times over
+ * original_max_position positions. pos is the row's absolute position.
+ * Errors: theta <= 1, a non-finite or non-positive factor or
+ * attention_factor, original_max_position < 1, beta_fast <= beta_slow or
+ * beta_slow <= 0 (with factor > 1), a negative or non-finite eps:
+ * INVALID_ARG. */
+typedef struct duo_rope {
+  float theta;
+  float factor;                   /* <= 1: plain RoPE */
+  int32_t original_max_position;
+  float beta_fast, beta_slow;
+  float attention_factor;
+} duo_rope;
+
+typedef struct duo_prologue {
+  const float* norm_weight;
+  float norm_eps;
+  const duo_rope* rope;
+} duo_prologue;
+
 /* Optional output epilogue of the attention calls (pass NULL for none).
  * sink_logits : device float [Hq] or NULL. Attention sink of a sliding layer
  *               (Laguna-M.1-8bit post, sliding-window optimisations: a
@@ -146,10 +186,13 @@ typedef struct duo_epilogue {
  *                a contiguous cache, so a wrong bound cannot corrupt memory.
  * When one call brings more positions than a ring holds, only the newest
  * positions of each slot are written, so every slot has exactly one writer.
- * Bit copy: no rounding. */
+ * Bit copy, no rounding, unless k_prologue is given: then each written K row
+ * is the bf16 (round to nearest even) of the prologue of k_new at its
+ * position; V stays a bit copy. */
 int duo_kv_append(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch,
                   const void* k_new, const void* v_new, int32_t num_tokens,
-                  const int32_t* start_pos, int64_t max_end_pos, void* stream);
+                  const int32_t* start_pos, int64_t max_end_pos, const duo_prologue* k_prologue,
+                  void* stream);
 
 /* Prefill attention for a chunk of num_tokens query positions
  * [start_pos, start_pos + num_tokens) of every sequence in the batch.
@@ -161,13 +204,16 @@ int duo_kv_append(const duo_layer* layer, const duo_kv_cache* cache, int32_t bat
  * out : device [batch, num_tokens, Hq, 128] bf16 (round to nearest even).
  * lse : NULL or device float [batch, Hq, num_tokens], natural-log
  *       log-sum-exp of the scaled logits of each row.
+ * q_prologue : NULL or the RMSNorm / rotary embedding of q (duo_prologue),
+ *       applied as the query rows are loaded, at positions start_pos + t; k
+ *       must already hold the prologue's output (duo_qk_prologue).
  * epilogue : NULL or the attention sink / output gate (duo_epilogue); a
  *       per-element gate is [batch, num_tokens, Hq, 128], a per-head gate
  *       [batch, num_tokens, Hq]. */
 int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t batch,
                      const void* q, const void* k, const void* v, int32_t num_tokens,
-                     int64_t start_pos, void* out, float* lse, const duo_epilogue* epilogue,
-                     void* stream);
+                     int64_t start_pos, void* out, float* lse, const duo_prologue* q_prologue,
+                     const duo_epilogue* epilogue, void* stream);
 
 /* Decode attention: one query token per sequence at position seq_lens[b]-1,
  * whose K/V have already been appended (seq_lens counts them).
@@ -175,6 +221,7 @@ int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t b
  * seq_lens  : device int32 [batch], each in [1, max_seq_len]; a 0 entry
  *             yields a zero output row (lse = -inf, or the sink logit when
  *             the epilogue has one).
+ * q_prologue: NULL or duo_prologue, applied to q at position seq_lens[b] - 1.
  * epilogue  : NULL or duo_epilogue; gate [batch, Hq, 128] or [batch, Hq].
  * max_seq_len : host bound used to size the split-K grid.
  * out       : device [batch, Hq, 128] bf16.  lse: NULL or device float [batch, Hq].
@@ -189,7 +236,7 @@ int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t b
 int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch,
                     const void* q, const int32_t* seq_lens, int64_t max_seq_len,
                     void* out, float* lse, void* workspace, size_t workspace_bytes,
-                    const duo_epilogue* epilogue, void* stream);
+                    const duo_prologue* q_prologue, const duo_epilogue* epilogue, void* stream);
 
 /* Block decode: num_tokens consecutive query tokens per sequence, at
  * positions past_lens[b] .. past_lens[b] + num_tokens - 1 -- the block a
@@ -209,13 +256,15 @@ int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t b
  * num_tokens  : 1 .. 64.
  * workspace   : as for duo_attn_decode, of duo_attn_decode_block_workspace_bytes()
  *               bytes (zero-filled once before first use).
+ * q_prologue  : NULL or duo_prologue, applied to q at positions past_lens[b] + t;
+ *               k_new must already hold the prologue's output.
  * epilogue    : NULL or duo_epilogue; gate [batch, num_tokens, Hq, 128] or
  *               [batch, num_tokens, Hq]. */
 int duo_attn_decode_block(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch,
                           const void* q, const void* k_new, const void* v_new, int32_t num_tokens,
                           const int32_t* past_lens, int64_t max_past_len, void* out, float* lse,
-                          void* workspace, size_t workspace_bytes, const duo_epilogue* epilogue,
-                          void* stream);
+                          void* workspace, size_t workspace_bytes, const duo_prologue* q_prologue,
+                          const duo_epilogue* epilogue, void* stream);
 
 /* Workspace size for duo_attn_decode_block; 0 on invalid arguments. Host only. */
 size_t duo_attn_decode_block_workspace_bytes(const duo_layer* layer, int32_t batch,
@@ -224,6 +273,22 @@ size_t duo_attn_decode_block_workspace_bytes(const duo_layer* layer, int32_t bat
 /* Zero-fill a decode workspace (enqueued on `stream`; a small fill kernel, so
  * it is also safe under graph capture). */
 int duo_attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Host only: the angular frequency f_i (radians per position) of each of the
+ * 64 rotary pairs that the prologue uses for `rope` (YaRN blend included).
+ * freqs: host double [64]. */
+int duo_rope_frequencies(const duo_rope* rope, double* freqs);
+
+/* The prologue on its own: y[b, t, h, :] = bf16(prologue(x[b, t, h, :])) at
+ * position start_pos[b] + t (round to nearest even). Used for the K of a
+ * prefill chunk or a verify block, which the attention reads before it is
+ * appended (attend, then append; append it afterwards without a prologue).
+ * x, y      : device bf16 [batch, num_tokens, heads, 128], 16-byte aligned;
+ *             y == x works in place, other overlaps are undefined.
+ * start_pos : device int32 [batch].
+ * heads     : 1 .. 4096. One HBM pass over x and y. */
+int duo_qk_prologue(const duo_prologue* prologue, int32_t batch, int32_t num_tokens, int32_t heads,
+                    const void* x, void* y, const int32_t* start_pos, void* stream);
 
 /* Workspace size for duo_attn_decode; 0 on invalid arguments. Host only. */
 size_t duo_attn_decode_workspace_bytes(const duo_layer* layer, int32_t batch,

@@ -222,7 +222,7 @@ def test_epilogue_validation_errors(lib):
     for sl, gate, mode in ((0, 0, 1), (0, 0x800000, 0), (0, 0x800000, 3)):
         e = g._Epilogue(sl, gate, mode)
         rc = lib.load().duo_attn_prefill(ctypes.byref(Layer()._c()), None, 1, q.data_ptr(), kv.data_ptr(),
-                                         kv.data_ptr(), 8, 0, o.data_ptr(), None, ctypes.byref(e), None)
+                                         kv.data_ptr(), 8, 0, o.data_ptr(), None, None, ctypes.byref(e), None)
         assert rc == -1, (sl, gate, mode)
         assert "gate" in lib.load().duo_last_error().decode()
     # decode and block decode check the epilogue too
@@ -235,3 +235,43 @@ def test_epilogue_validation_errors(lib):
     wsb = FakeTensor((g.decode_block_workspace_bytes(Layer(), 4, 2, 1000) // 4,), 0x600000)
     assert _err(g.attn_decode_block, Layer(), FakeCache(cap=1000), qb, kvb, kvb, sl_, 1000, qb, wsb,
                 sink_logits=FakeTensor((48,), 0x700001), stream=0) == -1
+
+
+def test_prologue_validation_errors(lib):
+    """Bad prologues are refused on the host before any launch."""
+    x = FakeTensor((2, 4, 8, 128))
+    sp = FakeTensor((2,))
+    bad = [
+        g.Prologue(rope=g.Rope(theta=1.0)),
+        g.Prologue(rope=g.Rope(factor=float("nan"))),
+        g.Prologue(rope=g.Rope(attention_factor=0.0)),
+        g.Prologue(rope=g.Rope(beta_fast=1.0, beta_slow=1.0)),
+        g.Prologue(rope=g.Rope(original_max_position=0)),
+        g.Prologue(eps=-1.0),
+        g.Prologue(norm_weight=FakeTensor((128,), 0x700002)),
+    ]
+    for pro in bad:
+        assert _err(g.qk_prologue, pro, x, sp, stream=0) == -1, pro
+        assert _err(g.kv_append, Layer(), FakeCache(), x, x, sp, max_end_pos=16, k_prologue=pro, stream=0) == -1
+        q = FakeTensor((2, 4, 48, 128))
+        assert _err(g.attn_prefill, Layer(), q, x, x, q, q_prologue=pro, stream=0) == -1
+    # plain RoPE with factor <= 1 needs no YaRN fields
+    assert len(g.rope_frequencies(g.Rope(theta=10000.0, factor=1.0, original_max_position=0, beta_fast=0,
+                                         beta_slow=0))) == 64
+    assert _err(g.qk_prologue, g.Prologue(), FakeTensor((2, 4, 8, 128), 0x100008), sp, stream=0) == -1
+
+
+@pytest.mark.parametrize("rope", [dict(), dict(factor=1.0), dict(theta=10000.0, factor=8.0, original_max_position=2048,
+                                                                  beta_fast=32.0, beta_slow=1.0),
+                                  dict(factor=4.0, beta_fast=2.0, beta_slow=1.5)])
+def test_rope_frequencies_match_the_oracle(lib, rope):
+    """The library's host-computed rotary frequencies (YaRN blend included)
+    against the oracle's, two independent implementations of the same
+    published formula."""
+    import oracle
+    r = g.Rope(**rope)
+    got = np.array(g.rope_frequencies(r))
+    want = oracle.rope_frequencies(np.float64(np.float32(r.theta)), float(np.float32(r.factor)),
+                                   r.original_max_position, float(np.float32(r.beta_fast)),
+                                   float(np.float32(r.beta_slow)))
+    assert np.allclose(got, want, rtol=1e-13, atol=0)
