@@ -100,7 +100,44 @@ def bench_prefill(torch, G, wl, timer, warmup, steps):
     flops = G.prefill_flops(layer, w.batch, w.seq)
     log("prefill: timing")
     ms = timer.run(lambda i: G.attn_prefill(layer, qd, kd, vd, out), warmup, steps)
-    return w, (q, k, v), flops, ms
+    return w, (q, k, v), flops, ms, (layer, qd, kd, vd, out)
+
+
+def bench_prologue_epilogue(torch, G, wl, timer, warmup, steps, w, flops, base_ms, devs):
+    """The optional prologue (RMSNorm + YaRN RoPE of q fused into the query
+    loads; the standalone kernel; K through kv_append's prologue) and
+    epilogue (sink logits + per-element output gate) on the headline prefill
+    workload, beside the plain call."""
+    layer, qd, kd, vd, out = devs
+    B, T = w.batch, w.seq
+    g = torch.Generator(device="cuda")
+    g.manual_seed(w.seed)
+    wq = 1 + 0.3 * torch.randn(128, device="cuda", generator=g)
+    wk = 1 + 0.3 * torch.randn(128, device="cuda", generator=g)
+    pq = G.Prologue(norm_weight=wq, rope=G.Rope())
+    pk = G.Prologue(norm_weight=wk, rope=G.Rope())
+    sink = torch.rand(w.hq, device="cuda", generator=g) * 10 - 2
+    gate = torch.randn(out.shape, device="cuda", generator=g).to(torch.bfloat16)
+    r = {"workload": w.name, "rope": "YaRN theta 500000 factor 64 (orig 4096, beta 64/1) + RMSNorm"}
+    log("prologue/epilogue: timing")
+    ms = timer.run(lambda i: G.attn_prefill(layer, qd, kd, vd, out, q_prologue=pq), warmup, steps)
+    r["prefill_q_prologue"] = {"ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12, "over_plain": ms / base_ms}
+    ms = timer.run(lambda i: G.attn_prefill(layer, qd, kd, vd, out, sink_logits=sink, gate=gate), warmup, steps)
+    r["prefill_sink_gate"] = {"ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12, "over_plain": ms / base_ms}
+    sp = torch.zeros(B, dtype=torch.int32, device="cuda")
+    y = torch.empty_like(qd)
+    for name, x, yy in (("qk_prologue_q", qd, y), ("qk_prologue_k", kd, torch.empty_like(kd))):
+        ms = timer.run(lambda i: G.qk_prologue(pk, x, sp, yy), warmup, steps)
+        nb = 2 * x.numel() * 2
+        r[name] = {"shape": list(x.shape), "ms": ms, "bytes": nb, "GB/s": nb / (ms * 1e-3) / 1e9,
+                   "frac_hbm_peak": nb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+    cache = G.KVCache(layer, B, T, zero=False)
+    nb = 4 * kd.numel() * 2          # read K and V, write K and V
+    for name, pro in (("kv_append_plain", None), ("kv_append_k_prologue", pk)):
+        ms = timer.run(lambda i: G.kv_append(layer, cache, kd, vd, sp, max_end_pos=T, k_prologue=pro),
+                       warmup, steps)
+        r[name] = {"ms": ms, "bytes": nb, "GB/s": nb / (ms * 1e-3) / 1e9}
+    return r
 
 
 def bench_decode_sliding(torch, G, wl, timer, warmup, steps, replicas=8):
@@ -127,7 +164,12 @@ def bench_decode_sliding(torch, G, wl, timer, warmup, steps, replicas=8):
     nbytes = int(sum(min(int(x), w.window) for x in L)) * w.hkv * 128 * 2 * 2
     log("decode sliding: timing")
     ms = timer.run(lambda i: G.attn_decode(layer, caches[i % replicas], q, sl, maxlen, out, ws), warmup, steps)
-    return w, nbytes, ms, replicas
+    stats = dict(timer.last)
+    pro = G.Prologue(norm_weight=torch.ones(128, device="cuda"), rope=G.Rope())
+    ms_pro = timer.run(lambda i: G.attn_decode(layer, caches[i % replicas], q, sl, maxlen, out, ws, q_prologue=pro),
+                       warmup, steps)
+    timer.last = stats
+    return w, nbytes, ms, replicas, ms_pro
 
 
 def bench_decode_duo(torch, G, wl, timer, warmup, steps, replicas=2):
@@ -324,7 +366,7 @@ def main():
 
     w2 = qkv = None
     if "prefill" in sections:
-        w2, qkv, flops, ms = bench_prefill(torch, G, wl, timer, args.warmup, args.steps)
+        w2, qkv, flops, ms, devs = bench_prefill(torch, G, wl, timer, args.warmup, args.steps)
         tflops = flops / (ms * 1e-3) / 1e12
         res["value"] = tflops
         res["ms_per_step"] = ms
@@ -342,14 +384,20 @@ def main():
                            "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": tflops / PEAK_MFMA_BF16_TFLOPS, "traffic": traffic}
         log(f"prefill: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
+        last = dict(timer.last)
+        res["prologue_epilogue"] = bench_prologue_epilogue(torch, G, wl, timer, args.warmup, args.steps, w2, flops,
+                                                           ms, devs)
+        timer.last = last
+        del devs
 
     if "decode" in sections:
         d = {}
-        w3, nb3, ms3, rep3 = bench_decode_sliding(torch, G, wl, timer, args.warmup, args.steps)
+        w3, nb3, ms3, rep3, ms3p = bench_decode_sliding(torch, G, wl, timer, args.warmup, args.steps)
         gbs3 = nb3 / (ms3 * 1e-3) / 1e9
         d["sliding_window"] = {"workload": w3.name, "kv_bytes": nb3, "ms": ms3, "GB/s": gbs3,
                                "frac_hbm_peak": gbs3 / PEAK_HBM_GBS, "cache_replicas": rep3,
-                               "ms_median": timer.last["median_ms"], "ms_min": timer.last["min_ms"]}
+                               "ms_median": timer.last["median_ms"], "ms_min": timer.last["min_ms"],
+                               "ms_with_q_prologue": ms3p}
         log(f"decode sliding: {ms3 * 1e3:.1f} us, {gbs3:.0f} GB/s")
         w4, nb4, ms4, rep4, mask4, sumL, blk4 = bench_decode_duo(torch, G, wl, timer, args.warmup, args.steps)
         gbs4 = nb4 / (ms4 * 1e-3) / 1e9
