@@ -300,7 +300,7 @@ def kernel_source_hash() -> str:
     version of the kernel are not reported."""
     import hashlib
     h = hashlib.sha256()
-    for f in ("prefill.hip", "duo_internal.h", "mfma_common.h"):
+    for f in ("prefill.hip", "duo_internal.h", "mfma_common.h", "qk_prologue.h"):
         h.update(open(os.path.join(HERE, "gqa_sliding_window_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -340,9 +340,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sections", default="prefill,decode,chunked",
-                    help="comma list of prefill, decode, chunked, copy (copy = counter "
-                         "calibration: a plain 1 GiB device copy)")
+    ap.add_argument("--sections", default="prefill,prologue,decode,chunked",
+                    help="comma list of prefill, prologue (needs prefill), decode, chunked, copy "
+                         "(copy = counter calibration: a plain 1 GiB device copy)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -384,10 +384,9 @@ def main():
                            "peak": PEAK_MFMA_BF16_TFLOPS, "unit": "TFLOP/s",
                            "frac": tflops / PEAK_MFMA_BF16_TFLOPS, "traffic": traffic}
         log(f"prefill: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
-        last = dict(timer.last)
-        res["prologue_epilogue"] = bench_prologue_epilogue(torch, G, wl, timer, args.warmup, args.steps, w2, flops,
-                                                           ms, devs)
-        timer.last = last
+        if "prologue" in sections:
+            res["prologue_epilogue"] = bench_prologue_epilogue(torch, G, wl, timer, args.warmup, args.steps, w2,
+                                                               flops, ms, devs)
         del devs
 
     if "decode" in sections:
