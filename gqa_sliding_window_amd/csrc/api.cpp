@@ -241,14 +241,18 @@ int build_decode(const Layer& L, int32_t batch, int64_t max_seq_len, int64_t mai
   p->scale_log2 = L.scale * 1.4426950408889634f;
   p->window = L.main_ring ? L.window : 0;
   p->T = block_tokens > 0 ? block_tokens : 1;
-  p->n_cb = (p->T * L.group + 15) / 16;
+  // column blocks per work item: 16 columns (one MFMA width) for the
+  // single-token decode, 32 (two halves sharing each K/V tile) for a block
+  p->n_cb = block_tokens > 0 ? (p->T * L.group + 31) / 32 : (L.group + 15) / 16;
   const int64_t extra = block_tokens;  // the block's own keys follow the cached ones
   const int64_t keys_main = (L.main_ring ? (max_seq_len < L.window ? max_seq_len : L.window) : max_seq_len) + extra;
   const int64_t sr = (int64_t)L.sink + L.recent;
   const int64_t keys_stream = (max_seq_len < sr ? max_seq_len : sr) + extra;
   const int64_t total = (int64_t)batch * (L.plan.n_main * keys_main + L.plan.n_stream * keys_stream);
   const int64_t unit = (int64_t)kDecodeKeys * kDecodeWaves;
-  int64_t split = (total + kDecodeTargetItems - 1) / kDecodeTargetItems;
+  // (a block decode launches n_cb workgroups per item: the target counts workgroups)
+  const int64_t target = kDecodeTargetItems / p->n_cb > 8 ? kDecodeTargetItems / p->n_cb : 8;
+  int64_t split = (total + target - 1) / target;
   if (split < kDecodeMinSplit) split = kDecodeMinSplit;
   const int64_t longest = keys_main > keys_stream ? keys_main : keys_stream;
   const int64_t min_for_cap = (longest + kDecodeMaxSplits - 1) / kDecodeMaxSplits;

@@ -48,12 +48,14 @@ __device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t*
 
 // Block decode: key index k < n_valid is cache slot k, k >= n_valid is row
 // k - n_valid of the block's own K/V (stride `bstride` elements per token).
+// This wave loads rows ld_row + 4 j (j < kJ) of the tile starting at k0.
+template <int kJ>
 __device__ __forceinline__ void load_tile_block(const uint16_t* kbase, const uint16_t* vbase,
                                                 const uint16_t* kblk, const uint16_t* vblk, int64_t bstride,
                                                 int64_t n_valid, int64_t k0, int64_t k_end, int ld_row,
-                                                int ld_chunk, u32x4 (&stK)[8], u32x4 (&stV)[8]) {
+                                                int ld_chunk, u32x4 (&stK)[kJ], u32x4 (&stV)[kJ]) {
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < kJ; ++j) {
     int64_t key = k0 + ld_row + 4 * j;
     key = key < k_end ? key : k_end - 1;
     const bool cached = key < n_valid;
@@ -103,6 +105,19 @@ __device__ __forceinline__ void stage_tile(uint16_t* sK, uint16_t* sV, int ld_ro
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Block decode: this wave's rows ld_row + 4 j (j < 4, ld_row in [16 h,
+// 16 h + 4)) into the key slot's shared tile; the workgroup barrier that
+// follows orders them before the reads.
+__device__ __forceinline__ void stage_rows(uint16_t* sK, uint16_t* sV, int ld_row, int ld_chunk,
+                                           const u32x4 (&stK)[4], const u32x4 (&stV)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int off = (ld_row + 4 * j) * kDPitch + ld_chunk * 8;
+    *reinterpret_cast<u32x4*>(&sK[off]) = stK[j];
+    *reinterpret_cast<u32x4*>(&sV[off]) = stV[j];
+  }
 }
 
 // One 32-key tile from LDS: S^T = K Q^T, mask slots >= k_end, online softmax
@@ -208,12 +223,25 @@ __device__ __forceinline__ void write_out_pair(const DecodeParams& p, int64_t bh
 }
 
 // One work item: (sequence, KV head, split) and, for the block decode, one
-// 16-wide block of its (query token, query head) columns.
+// 32-wide block of its (query token, query head) columns.
+//
+// Single-token decode: 4 waves, each streaming its own 32-key tiles through a
+// private LDS tile, two tiles in flight in registers.
+// Block decode: 8 waves in 4 key slots x 2 column halves of 16. The two
+// waves of a slot load half of each 32-key tile each (4 tiles in flight in
+// registers: the same bytes in flight per CU as the single-token kernel)
+// into the slot's shared LDS tile, and each attends it for its own 16
+// columns, so the cache is streamed once for 32 columns.
 template <bool kBlock>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
-  // K/V tiles of the 4 waves; reused after the key loop for the combine/merge.
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kDecodeWaves * 2 * kTileElems];
-  __shared__ float s_ml[kDecodeWaves][16][2];
+  constexpr int kNH = kBlock ? 2 : 1;          // 16-column halves per work item
+  constexpr int kCols = 16 * kNH;
+  constexpr int kNW = kDecodeWaves * kNH;      // waves per workgroup
+  constexpr int kThreads = 64 * kNW;
+  // K/V tiles (single token: one per wave; block: two per key slot, used
+  // alternately); reused after the key loop for the combine/merge.
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kDecodeWaves * 2 * kNH * kTileElems];
+  __shared__ float s_ml[kDecodeWaves][kCols][2];
   __shared__ int s_last;
 
   // Block decode: workgroup i runs on XCD i % 8 (round-robin dispatch); the
@@ -229,6 +257,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   const DecodeItem it = decode_item(p, item);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
+  const int slot = wave % kDecodeWaves;  // key slot: tiles k_begin + 32 (slot + 4 t)
+  const int half = wave / kDecodeWaves;  // column half of the block decode
   const int lane = tid & 63;
   const int r16 = lane & 15;
   const int g = lane >> 4;
@@ -247,8 +277,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 
   // Columns of this item: (token t, head g) = (c / G, c % G), c in
   // [col0, col0 + n_cols); output row of column c.
-  const int col0 = 16 * cb;
-  const int n_cols = min(16, T * G - col0);
+  const int col0 = kCols * cb;
+  const int n_cols = min(kCols, T * G - col0);
+  const int n_half = (n_cols + 15) / 16;  // halves holding columns (uniform)
   auto row_of = [&](int c) -> int64_t {
     const int cc = col0 + c;
     return kBlock ? (((int64_t)it.b * T + cc / G) * p.hq + (int64_t)it.kvh * G + cc % G)
@@ -259,7 +290,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   if (it.split >= n_used) {
     // empty split; split 0 of a sequence without keys writes the zero rows
     if (it.split == 0) {
-      for (int e = tid; e < n_cols * (kD / 2); e += 256) {
+      for (int e = tid; e < n_cols * (kD / 2); e += kThreads) {
         const int64_t row = row_of(e / (kD / 2));
         *reinterpret_cast<uint32_t*>(p.out + row * kD + 2 * (e % (kD / 2))) = 0u;
         if (p.lse != nullptr && (e % (kD / 2)) == 0)  // the sink alone, if any, forms the normaliser
@@ -281,11 +312,13 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     vbase = p.v_main + off;
   }
 
-  // Q fragments: lane column r16 (zero beyond the item's columns).
+  // Q fragments of this wave's half: lane column hc = 16 half + r16 (zero
+  // beyond the item's columns).
+  const int hc = 16 * half + r16;
   bf16x8 qf[4];
   {
-    const bool ok = r16 < n_cols;
-    const uint16_t* src = p.q + row_of(ok ? r16 : 0) * kD + 8 * g;
+    const bool ok = hc < n_cols;
+    const uint16_t* src = p.q + row_of(ok ? hc : 0) * kD + 8 * g;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds) {
       u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(src + 32 * ds) : u32x4{0u, 0u, 0u, 0u};
@@ -293,7 +326,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     }
     // RMSNorm + RoPE of q: the single-token query sits at len - 1, block
     // token t at past + t.
-    if (p.qpro_on) prologue_frag(qf, kBlock ? (int)len + (col0 + r16) / G : (int)len - 1, g, p.qpro);
+    if (p.qpro_on) prologue_frag(qf, kBlock ? (int)len + (col0 + hc) / G : (int)len - 1, g, p.qpro);
   }
 
   // Block decode: visibility of each key for this lane's query token.
@@ -304,7 +337,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   const int64_t bstride = (int64_t)p.hkv * kD;
   if (kBlock) {
     const int past = len > 0 ? (int)len : 0;  // cached positions [0, past)
-    const int t = (r16 < n_cols ? col0 + r16 : col0) / G;
+    const int t = (hc < n_cols ? col0 + hc : col0) / G;
     bv.n_valid = n_valid;
     bv.past = past;
     bv.q_pos = past + t;
@@ -333,71 +366,106 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     vblk = p.v_new + ((int64_t)it.b * T * p.hkv + it.kvh) * kD;
   }
 
-  uint16_t* sK = smem + wave * 2 * kTileElems;
-  uint16_t* sV = sK + kTileElems;
-  const int ld_row = lane >> 4;
-  const int ld_chunk = lane & 15;
-
   const float c = p.scale_log2;
   float m = kNegInf, l = 0.f;
   f32x4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto load = [&](int64_t k0, u32x4 (&bk)[8], u32x4 (&bvv)[8]) {
-    if (kBlock)
-      load_tile_block(kbase, vbase, kblk, vblk, bstride, n_valid, k0, k_end, ld_row, ld_chunk, bk, bvv);
-    else
-      load_tile(kbase, vbase, k0, k_end, ld_row, ld_chunk, bk, bvv);
-  };
-
-  // This wave's tiles start at k_begin + 32 * (wave + 4 t). Two tiles are kept
-  // in flight (register buffers A and B, used alternately). Loads are issued
-  // unconditionally so the wait counts stay exact: a tile past the split end
-  // reads the last valid key and is fully masked, leaving (m, l, o) unchanged.
+  // Tiles of key slot `slot` start at k_begin + 32 * (slot + 4 t). Loads are
+  // issued unconditionally so the wait counts stay exact: a tile past the
+  // split end reads the last valid key and is fully masked, leaving (m, l, o)
+  // unchanged.
   const int64_t stride = (int64_t)kDecodeKeys * kDecodeWaves;
-  const int64_t first = k_begin + (int64_t)kDecodeKeys * wave;
-  const int64_t nt = first < k_end ? (k_end - first + stride - 1) / stride : 0;
-  u32x4 aK[8], aV[8], bK[8], bV[8];
-  // (scheduling barriers keep each tile's 16 loads contiguous in issue order,
-  // so waiting for one buffer never waits for the other)
-  load(first, aK, aV);
-  __builtin_amdgcn_sched_barrier(0);
-  load(first + stride, bK, bV);
-  __builtin_amdgcn_sched_barrier(0);
-  for (int64_t t = 0; t < nt; t += 2) {
-    const int64_t k0 = first + t * stride;
-    stage_tile(sK, sV, ld_row, ld_chunk, aK, aV);
+  const int64_t first = k_begin + (int64_t)kDecodeKeys * slot;
+  const int ld_chunk = lane & 15;
+  if (!kBlock) {
+    uint16_t* sK = smem + wave * 2 * kTileElems;
+    uint16_t* sV = sK + kTileElems;
+    const int ld_row = lane >> 4;
+    const int64_t nt = first < k_end ? (k_end - first + stride - 1) / stride : 0;
+    // Two tiles in flight (register buffers A and B, used alternately).
+    // (scheduling barriers keep each tile's 16 loads contiguous in issue
+    // order, so waiting for one buffer never waits for the other)
+    u32x4 aK[8], aV[8], bK[8], bV[8];
+    load_tile(kbase, vbase, first, k_end, ld_row, ld_chunk, aK, aV);
     __builtin_amdgcn_sched_barrier(0);
-    load(k0 + 2 * stride, aK, aV);
+    load_tile(kbase, vbase, first + stride, k_end, ld_row, ld_chunk, bK, bV);
     __builtin_amdgcn_sched_barrier(0);
-    attend_tile<kBlock>(sK, sV, qf, k0, k_end, c, r16, g, m, l, o, bv, mask_all);
-    __builtin_amdgcn_sched_barrier(0);
-    stage_tile(sK, sV, ld_row, ld_chunk, bK, bV);
-    __builtin_amdgcn_sched_barrier(0);
-    load(k0 + 3 * stride, bK, bV);
-    __builtin_amdgcn_sched_barrier(0);
-    attend_tile<kBlock>(sK, sV, qf, k0 + stride, k_end, c, r16, g, m, l, o, bv, mask_all);
-    __builtin_amdgcn_sched_barrier(0);
+    for (int64_t t = 0; t < nt; t += 2) {
+      const int64_t k0 = first + t * stride;
+      stage_tile(sK, sV, ld_row, ld_chunk, aK, aV);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(kbase, vbase, k0 + 2 * stride, k_end, ld_row, ld_chunk, aK, aV);
+      __builtin_amdgcn_sched_barrier(0);
+      attend_tile<kBlock>(sK, sV, qf, k0, k_end, c, r16, g, m, l, o, bv, mask_all);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_tile(sK, sV, ld_row, ld_chunk, bK, bV);
+      __builtin_amdgcn_sched_barrier(0);
+      load_tile(kbase, vbase, k0 + 3 * stride, k_end, ld_row, ld_chunk, bK, bV);
+      __builtin_amdgcn_sched_barrier(0);
+      attend_tile<kBlock>(sK, sV, qf, k0 + stride, k_end, c, r16, g, m, l, o, bv, mask_all);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // The slot's two LDS tiles, used alternately: one workgroup barrier per
+    // tile orders this tile's staging before its reads, and every read of
+    // the other tile (two tiles back) before its next staging.
+    uint16_t* sK0 = smem + slot * 4 * kTileElems;
+    uint16_t* sV0 = sK0 + kTileElems;
+    uint16_t* sK1 = sV0 + kTileElems;
+    uint16_t* sV1 = sK1 + kTileElems;
+    const int ld_row = 16 * half + (lane >> 4);  // rows ld_row + 4 j, j < 4
+    // the same trip count in every wave (barriers): slot 0 has the most tiles
+    const int64_t nt = (k_end - k_begin + stride - 1) / stride;
+    u32x4 xK[4][4], xV[4][4];  // four half tiles in flight
+    auto load = [&](int64_t k0, u32x4 (&bk)[4], u32x4 (&bvv)[4]) {
+      load_tile_block<4>(kbase, vbase, kblk, vblk, bstride, n_valid, k0, k_end, ld_row, ld_chunk, bk, bvv);
+    };
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      load(first + i * stride, xK[i], xV[i]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    auto step = [&](int64_t t, u32x4 (&bk)[4], u32x4 (&bvv)[4], uint16_t* sK, uint16_t* sV) {
+      const int64_t k0 = first + t * stride;
+      stage_rows(sK, sV, ld_row, ld_chunk, bk, bvv);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      load(k0 + 4 * stride, bk, bvv);
+      __builtin_amdgcn_sched_barrier(0);
+      if (half < n_half)  // a half without columns only helps load and stage
+        attend_tile<kBlock>(sK, sV, qf, k0, k_end, c, r16, g, m, l, o, bv, mask_all);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int64_t t = 0; t < nt; t += 4) {
+      step(t, xK[0], xV[0], sK0, sV0);
+      if (t + 1 >= nt) break;
+      step(t + 1, xK[1], xV[1], sK1, sV1);
+      if (t + 2 >= nt) break;
+      step(t + 2, xK[2], xV[2], sK0, sV0);
+      if (t + 3 >= nt) break;
+      step(t + 3, xK[3], xV[3], sK1, sV1);
+    }
   }
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
 
-  // ---- combine the 4 waves: acc[w][col][dim] in LDS (reuses the tile area)
+  // ---- combine the 4 key slots: acc[slot][col][dim] in LDS (reuses the tile area)
   __syncthreads();
-  float* comb = reinterpret_cast<float*>(smem);  // [4][16][128] floats = 32 KB
+  float* comb = reinterpret_cast<float*>(smem);  // [4][kCols][128] floats
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt)
-    *reinterpret_cast<f32x4*>(&comb[(wave * 16 + r16) * kD + 16 * dt + 4 * g]) = o[dt];
+    *reinterpret_cast<f32x4*>(&comb[(slot * kCols + hc) * kD + 16 * dt + 4 * g]) = o[dt];
   if (g == 0) {
-    s_ml[wave][r16][0] = m;
-    s_ml[wave][r16][1] = l;
+    s_ml[slot][hc][0] = m;
+    s_ml[slot][hc][1] = l;
   }
   __syncthreads();
 
   // thread -> (column, dim pair) of the item's columns; 64 threads per column
   const bool single = (n_used == 1);
-  for (int e = tid; e < n_cols * (kD / 2); e += 256) {
+  for (int e = tid; e < n_cols * (kD / 2); e += kThreads) {
     const int col = e / (kD / 2);
     const int dim = 2 * (e % (kD / 2));
     float M = kNegInf;
@@ -409,8 +477,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       const float mw = s_ml[w][col][0];
       const float sc = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
       L += sc * s_ml[w][col][1];
-      a0 += sc * comb[(w * 16 + col) * kD + dim];
-      a1 += sc * comb[(w * 16 + col) * kD + dim + 1];
+      a0 += sc * comb[(w * kCols + col) * kD + dim];
+      a1 += sc * comb[(w * kCols + col) * kD + dim + 1];
     }
     const int64_t row = row_of(col);
     if (single) {
@@ -418,12 +486,12 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       write_out_pair(p, row, dim, a0, a1, rn.inv);
       if (p.lse != nullptr && dim == 0) p.lse[row] = rn.lse;
     } else {
-      const int64_t slot = row * p.n_split_max + it.split;
-      coherent_store(p.ws_acc + slot * kD + dim, a0);
-      coherent_store(p.ws_acc + slot * kD + dim + 1, a1);
+      const int64_t wslot = row * p.n_split_max + it.split;
+      coherent_store(p.ws_acc + wslot * kD + dim, a0);
+      coherent_store(p.ws_acc + wslot * kD + dim + 1, a1);
       if (dim == 0) {
-        coherent_store(p.ws_ml + slot * 2 + 0, M);
-        coherent_store(p.ws_ml + slot * 2 + 1, L);
+        coherent_store(p.ws_ml + wslot * 2 + 0, M);
+        coherent_store(p.ws_ml + wslot * 2 + 1, L);
       }
     }
   }
@@ -441,96 +509,102 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   __syncthreads();
   if (!s_last) return;
 
-  // (max, sum) of every (column, split) into LDS with all loads in flight,
-  // then per-column max / weights / normaliser, then the weighted sum of the
-  // partial outputs (wave w takes splits w, w+4, ...; 4 splits per batch).
+  // Merge, 16 columns at a time: (max, sum) of every (column, split) into
+  // LDS with all loads in flight, then per-column max / weights / normaliser,
+  // then the weighted sum of the partial outputs (wave w takes splits w,
+  // w + kNW, ...; 4 splits per batch).
   float* s_m = reinterpret_cast<float*>(smem);  // [16][kDecodeMaxSplits]
   float* s_w = s_m + 16 * kDecodeMaxSplits;       // [16][kDecodeMaxSplits] weights
   float* s_L = s_w + 16 * kDecodeMaxSplits;       // [16] output factors (1 / normaliser)
-  float* red = s_L + 16;                          // [4][16][128]
-  for (int e = tid; e < n_cols * n_used; e += 256) {
-    const int h = e / n_used, sp = e % n_used;
-    const float* ml = p.ws_ml + (row_of(h) * p.n_split_max + sp) * 2;
-    s_m[h * kDecodeMaxSplits + sp] = coherent_load(ml);
-    s_w[h * kDecodeMaxSplits + sp] = coherent_load(ml + 1);
-  }
-  __syncthreads();
-  for (int h = wave; h < n_cols; h += kDecodeWaves) {
-    float M = kNegInf;
-    for (int sp = lane; sp < n_used; sp += 64) M = fmaxf(M, s_m[h * kDecodeMaxSplits + sp]);
-#pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
-    float L = 0.f;
-    for (int sp = lane; sp < n_used; sp += 64) {
-      const float ms = s_m[h * kDecodeMaxSplits + sp];
-      const float w = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
-      L += w * s_w[h * kDecodeMaxSplits + sp];
-      s_w[h * kDecodeMaxSplits + sp] = w;
+  float* red = s_L + 16;                          // [kNW][16][128]
+  for (int hb = 0; hb < n_half; ++hb) {
+    const int c0 = 16 * hb;                       // first column of this half
+    const int nc = min(16, n_cols - c0);
+    if (hb > 0) __syncthreads();                  // the previous half is done with the LDS
+    for (int e = tid; e < nc * n_used; e += kThreads) {
+      const int h = e / n_used, sp = e % n_used;
+      const float* ml = p.ws_ml + (row_of(c0 + h) * p.n_split_max + sp) * 2;
+      s_m[h * kDecodeMaxSplits + sp] = coherent_load(ml);
+      s_w[h * kDecodeMaxSplits + sp] = coherent_load(ml + 1);
     }
+    __syncthreads();
+    for (int h = wave; h < nc; h += kNW) {
+      float M = kNegInf;
+      for (int sp = lane; sp < n_used; sp += 64) M = fmaxf(M, s_m[h * kDecodeMaxSplits + sp]);
 #pragma unroll
-    for (int x = 32; x >= 1; x >>= 1) L += __shfl_xor(L, x);
-    if (lane == 0) {
-      const RowNorm rn = row_norm(M, L, p.sink_logits, head_of(h));
-      s_L[h] = rn.inv;
-      if (p.lse != nullptr) p.lse[row_of(h)] = rn.lse;
+      for (int x = 32; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x));
+      float L = 0.f;
+      for (int sp = lane; sp < n_used; sp += 64) {
+        const float ms = s_m[h * kDecodeMaxSplits + sp];
+        const float w = (ms == kNegInf) ? 0.f : fast_exp2(ms - M);
+        L += w * s_w[h * kDecodeMaxSplits + sp];
+        s_w[h * kDecodeMaxSplits + sp] = w;
+      }
+#pragma unroll
+      for (int x = 32; x >= 1; x >>= 1) L += __shfl_xor(L, x);
+      if (lane == 0) {
+        const RowNorm rn = row_norm(M, L, p.sink_logits, head_of(c0 + h));
+        s_L[h] = rn.inv;
+        if (p.lse != nullptr) p.lse[row_of(c0 + h)] = rn.lse;
+      }
     }
-  }
-  __syncthreads();
-  float acc[kMaxGroup][2];
+    __syncthreads();
+    float acc[kMaxGroup][2];
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) acc[h][0] = acc[h][1] = 0.f;
-  constexpr int kBatch = 4;
-  for (int sp0 = wave; sp0 < n_used; sp0 += kDecodeWaves * kBatch) {
-    float v[kBatch][kMaxGroup][2];
+    for (int h = 0; h < kMaxGroup; ++h) acc[h][0] = acc[h][1] = 0.f;
+    constexpr int kBatch = 4;
+    for (int sp0 = wave; sp0 < n_used; sp0 += kNW * kBatch) {
+      float v[kBatch][kMaxGroup][2];
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int sp = sp0 + u * kDecodeWaves;
+      for (int u = 0; u < kBatch; ++u) {
+        const int sp = sp0 + u * kNW;
 #pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        if (h < n_cols && sp < n_used) {
-          const float* src = p.ws_acc + (row_of(h) * p.n_split_max + sp) * kD + 2 * lane;
-          v[u][h][0] = coherent_load(src);
-          v[u][h][1] = coherent_load(src + 1);
+        for (int h = 0; h < kMaxGroup; ++h) {
+          if (h < nc && sp < n_used) {
+            const float* src = p.ws_acc + (row_of(c0 + h) * p.n_split_max + sp) * kD + 2 * lane;
+            v[u][h][0] = coherent_load(src);
+            v[u][h][1] = coherent_load(src + 1);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int sp = sp0 + u * kNW;
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) {
+          if (h < nc && sp < n_used) {
+            const float w = s_w[h * kDecodeMaxSplits + sp];
+            acc[h][0] += w * v[u][h][0];
+            acc[h][1] += w * v[u][h][1];
+          }
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < kBatch; ++u) {
-      const int sp = sp0 + u * kDecodeWaves;
-#pragma unroll
-      for (int h = 0; h < kMaxGroup; ++h) {
-        if (h < n_cols && sp < n_used) {
-          const float w = s_w[h * kDecodeMaxSplits + sp];
-          acc[h][0] += w * v[u][h][0];
-          acc[h][1] += w * v[u][h][1];
-        }
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h < nc) {
+        red[(wave * 16 + h) * kD + 2 * lane] = acc[h][0];
+        red[(wave * 16 + h) * kD + 2 * lane + 1] = acc[h][1];
       }
     }
-  }
+    __syncthreads();
+    for (int e = tid; e < nc * (kD / 2); e += kThreads) {
+      const int col = e / (kD / 2);
+      const int dim = 2 * (e % (kD / 2));
+      float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-  for (int h = 0; h < kMaxGroup; ++h) {
-    if (h < n_cols) {
-      red[(wave * 16 + h) * kD + 2 * lane] = acc[h][0];
-      red[(wave * 16 + h) * kD + 2 * lane + 1] = acc[h][1];
+      for (int w = 0; w < kNW; ++w) {
+        a0 += red[(w * 16 + col) * kD + dim];
+        a1 += red[(w * 16 + col) * kD + dim + 1];
+      }
+      write_out_pair(p, row_of(c0 + col), dim, a0, a1, s_L[col]);
     }
-  }
-  __syncthreads();
-  for (int e = tid; e < n_cols * (kD / 2); e += 256) {
-    const int col = e / (kD / 2);
-    const int dim = 2 * (e % (kD / 2));
-    float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
-      a0 += red[(w * 16 + col) * kD + dim];
-      a1 += red[(w * 16 + col) * kD + dim + 1];
-    }
-    write_out_pair(p, row_of(col), dim, a0, a1, s_L[col]);
   }
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
 }
 
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) { decode_body<false>(p); }
-__global__ __launch_bounds__(256, 2) void decode_block_kernel(DecodeParams p) { decode_body<true>(p); }
+__global__ __launch_bounds__(512, 1) void decode_block_kernel(DecodeParams p) { decode_body<true>(p); }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -544,7 +618,7 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
 
 hipError_t launch_decode_block(const DecodeParams& p, hipStream_t s) {
   const int64_t items8 = ((int64_t)p.n_items + kXcds - 1) / kXcds * kXcds;
-  if (p.n_items > 0) hipLaunchKernelGGL(decode_block_kernel, dim3((unsigned)(items8 * p.n_cb)), dim3(256), 0, s, p);
+  if (p.n_items > 0) hipLaunchKernelGGL(decode_block_kernel, dim3((unsigned)(items8 * p.n_cb)), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 

@@ -236,7 +236,8 @@ struct DecodeParams {
   int32_t n_main, n_stream;
   uint32_t stream_mask;
   int32_t T;             // query tokens per sequence (1 for the single-token decode)
-  int32_t n_cb;          // 16-wide MFMA column blocks per work item: ceil(T * G / 16)
+  int32_t n_cb;          // column blocks per work item: 1 (single token, G <= 16 columns) or
+                         // ceil(T * G / 32) (block decode: two 16-column MFMA halves per block)
   int32_t split_keys;
   int32_t n_split_main, n_split_stream, n_split_max;
   int32_t n_items_main, n_items;

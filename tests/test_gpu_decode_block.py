@@ -78,6 +78,8 @@ CASES = {
                           [0, 3, 4, 12, 13, 14, 40], 8),
     "all_streaming_T2": (dict(full_attention_heads=[0] * 8), [64, 319, 320, 1000], 2),
     "group16_T3": (dict(num_q_heads=32, num_kv_heads=2), [77, 1200], 3),
+    "duo_T7_partial_second_block": (dict(full_attention_heads=[0, 1, 0, 0, 0, 0, 0, 1]), [0, 5, 700, 3000], 7),
+    "group16_T64_largest_block": (dict(num_q_heads=32, num_kv_heads=2, kind=1, window=512), [0, 100, 2000], 64),
     "duo_sliding_layer_T5": (dict(kind=1, window=100, full_attention_heads=[1, 0], sink=5, recent=7,
                                   num_q_heads=4, num_kv_heads=2), [0, 6, 12, 99, 100, 101, 450], 5),
 }
