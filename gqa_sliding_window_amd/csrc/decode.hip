@@ -223,18 +223,19 @@ __device__ __forceinline__ void write_out_pair(const DecodeParams& p, int64_t bh
 }
 
 // One work item: (sequence, KV head, split) and, for the block decode, one
-// 32-wide block of its (query token, query head) columns.
+// block of 16 kNH of its (query token, query head) columns.
 //
-// Single-token decode: 4 waves, each streaming its own 32-key tiles through a
-// private LDS tile, two tiles in flight in registers.
-// Block decode: 8 waves in 4 key slots x 2 column halves of 16. The two
-// waves of a slot load half of each 32-key tile each (4 tiles in flight in
-// registers: the same bytes in flight per CU as the single-token kernel)
-// into the slot's shared LDS tile, and each attends it for its own 16
-// columns, so the cache is streamed once for 32 columns.
-template <bool kBlock>
+// kNH = 1 (the single-token decode, and a block of at most 16 columns): 4
+// waves, each streaming its own 32-key tiles through a private LDS tile, two
+// tiles in flight in registers.
+// kNH = 2 (a block of more columns): 8 waves in 4 key slots x 2 column halves
+// of 16. The two waves of a slot load half of each 32-key tile each (4 half
+// tiles in flight in registers: the same bytes in flight per CU as the
+// single-token kernel) into the slot's shared LDS tile, and each attends it
+// for its own 16 columns, so the cache is streamed once for 32 columns.
+template <bool kBlock, int kNH>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
-  constexpr int kNH = kBlock ? 2 : 1;          // 16-column halves per work item
+  static_assert(kNH == 1 || (kBlock && kNH == 2), "two halves only for the block decode");
   constexpr int kCols = 16 * kNH;
   constexpr int kNW = kDecodeWaves * kNH;      // waves per workgroup
   constexpr int kThreads = 64 * kNW;
@@ -379,7 +380,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   const int64_t stride = (int64_t)kDecodeKeys * kDecodeWaves;
   const int64_t first = k_begin + (int64_t)kDecodeKeys * slot;
   const int ld_chunk = lane & 15;
-  if (!kBlock) {
+  if (kNH == 1) {
     uint16_t* sK = smem + wave * 2 * kTileElems;
     uint16_t* sV = sK + kTileElems;
     const int ld_row = lane >> 4;
@@ -387,22 +388,28 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     // Two tiles in flight (register buffers A and B, used alternately).
     // (scheduling barriers keep each tile's 16 loads contiguous in issue
     // order, so waiting for one buffer never waits for the other)
+    auto load = [&](int64_t k0, u32x4 (&bk)[8], u32x4 (&bvv)[8]) {
+      if (kBlock)
+        load_tile_block<8>(kbase, vbase, kblk, vblk, bstride, n_valid, k0, k_end, ld_row, ld_chunk, bk, bvv);
+      else
+        load_tile(kbase, vbase, k0, k_end, ld_row, ld_chunk, bk, bvv);
+    };
     u32x4 aK[8], aV[8], bK[8], bV[8];
-    load_tile(kbase, vbase, first, k_end, ld_row, ld_chunk, aK, aV);
+    load(first, aK, aV);
     __builtin_amdgcn_sched_barrier(0);
-    load_tile(kbase, vbase, first + stride, k_end, ld_row, ld_chunk, bK, bV);
+    load(first + stride, bK, bV);
     __builtin_amdgcn_sched_barrier(0);
     for (int64_t t = 0; t < nt; t += 2) {
       const int64_t k0 = first + t * stride;
       stage_tile(sK, sV, ld_row, ld_chunk, aK, aV);
       __builtin_amdgcn_sched_barrier(0);
-      load_tile(kbase, vbase, k0 + 2 * stride, k_end, ld_row, ld_chunk, aK, aV);
+      load(k0 + 2 * stride, aK, aV);
       __builtin_amdgcn_sched_barrier(0);
       attend_tile<kBlock>(sK, sV, qf, k0, k_end, c, r16, g, m, l, o, bv, mask_all);
       __builtin_amdgcn_sched_barrier(0);
       stage_tile(sK, sV, ld_row, ld_chunk, bK, bV);
       __builtin_amdgcn_sched_barrier(0);
-      load_tile(kbase, vbase, k0 + 3 * stride, k_end, ld_row, ld_chunk, bK, bV);
+      load(k0 + 3 * stride, bK, bV);
       __builtin_amdgcn_sched_barrier(0);
       attend_tile<kBlock>(sK, sV, qf, k0 + stride, k_end, c, r16, g, m, l, o, bv, mask_all);
       __builtin_amdgcn_sched_barrier(0);
@@ -603,8 +610,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
 }
 
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) { decode_body<false>(p); }
-__global__ __launch_bounds__(512, 1) void decode_block_kernel(DecodeParams p) { decode_body<true>(p); }
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) { decode_body<false, 1>(p); }
+__global__ __launch_bounds__(256, 2) void decode_block16_kernel(DecodeParams p) { decode_body<true, 1>(p); }
+__global__ __launch_bounds__(512, 1) void decode_block_kernel(DecodeParams p) { decode_body<true, 2>(p); }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -618,7 +626,12 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
 
 hipError_t launch_decode_block(const DecodeParams& p, hipStream_t s) {
   const int64_t items8 = ((int64_t)p.n_items + kXcds - 1) / kXcds * kXcds;
-  if (p.n_items > 0) hipLaunchKernelGGL(decode_block_kernel, dim3((unsigned)(items8 * p.n_cb)), dim3(512), 0, s, p);
+  if (p.n_items > 0) {
+    if (p.T * p.group <= 16)  // one 16-column block: the 4-wave form
+      hipLaunchKernelGGL(decode_block16_kernel, dim3((unsigned)(items8 * p.n_cb)), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(decode_block_kernel, dim3((unsigned)(items8 * p.n_cb)), dim3(512), 0, s, p);
+  }
   return hipGetLastError();
 }
 
