@@ -14,9 +14,12 @@
 // Workgroup = 4 waves = one (sequence, KV head, split). The G query heads of
 // the KV head are the 16 MFMA columns (G <= 16): one pass over K/V serves the
 // whole group. Each wave streams its own interleaved 32-key tiles (16-byte
-// coalesced loads, one tile ahead in registers, a wave-private LDS tile for the
-// MFMA operand layouts: K row-major, V read transposed) and keeps its own
+// coalesced loads, two tiles ahead in registers, a wave-private LDS tile for
+// the MFMA operand layouts: K row-major, V read transposed) and keeps its own
 // running (max, sum, output); the waves are combined through LDS.
+// The block decode (T query tokens per sequence, attend then append) uses
+// the same body with (token, head) columns: up to 16 columns in this 4-wave
+// form, more in 32-column blocks of 8 waves (see decode_body).
 // A sequence whose keys fit one split is finished by its workgroup. Otherwise
 // each split stores its combined partial in the workspace and bumps the
 // group's arrival counter; the last workgroup to arrive merges all partials
