@@ -18,7 +18,13 @@
  *    full layers), mask-generation section (causal and sliding-window causal
  *    masks chosen per layer type).
  *  - SGLang cookbook "Laguna-XS-2.1", section 1 "Model Introduction": 48 Q / 8
- *    KV heads, window 512, 30 sliding + 10 full layers.
+ *    KV heads, window 512, 30 sliding + 10 full layers; DFlash speculative
+ *    decoding (the target verifies a drafted block in one pass).
+ *  - Blog post on Laguna-XS-2.1 sliding-window attention, section on its
+ *    optimisations: q/k RMSNorm before the rotary embedding, an optional
+ *    learnable attention-sink bias on sliding layers, output gating through
+ *    a g_proj projection. Blog post on Laguna-M.1-8bit, YaRN section: the
+ *    rotary parameters of full-attention layers.
  *
  * Visibility of key position j for a query at position i (G = Hq / Hkv, query
  * head h uses KV head h / G):
@@ -27,9 +33,10 @@
  *   streaming head (any layer):                      j <= i and (j < sink or j > i - recent)
  *
  * Conventions for every entry point:
- *  - All tensors are bfloat16 (16-bit bit patterns), row-major, densely
- *    packed, head_dim = 128, and 16-byte aligned. Device pointers are owned by
- *    the caller; the library never allocates, frees or retains them.
+ *  - Tensors are bfloat16 (16-bit bit patterns), row-major, densely packed,
+ *    head_dim = 128, and 16-byte aligned, except the float32 lse outputs,
+ *    sink logits and RMSNorm weights (4-byte aligned). Device pointers are
+ *    owned by the caller; the library never allocates, frees or retains them.
  *  - `stream` is a hipStream_t (NULL = the legacy default stream). Calls only
  *    enqueue work and return; results are visible after the stream is
  *    synchronised.
