@@ -134,3 +134,37 @@ def test_block_workspace_reuse_and_smaller_call(lib):
                           lse=l3)
     torch.cuda.synchronize()
     check_block(layer, past, T2, q[:, :T2], k, v, host_bits(o3), l3.cpu().numpy(), "reuse call 3 (T=3)")
+
+
+def test_block_decode_duo_workload_T4(lib):
+    """The verify-block launch the bench times: T = 4 tokens after the Duo
+    decode workload's contexts (batch 16, 48/8 heads, contexts U[32768,
+    131072], its Bernoulli(0.25) mask), every row against the oracle."""
+    import torch
+    w = wl.WORKLOADS[4]
+    T = 4
+    announce(f"decode block parity {w.name} T={T}")
+    mask = wl.duo_mask(w).tolist()
+    layer = lib.Layer(full_attention_heads=mask)
+    past = wl.context_lengths(w).tolist()
+    B, hq, hkv = w.batch, w.hq, w.hkv
+    ends = [p + T for p in past]
+    k = wl.normal_tokens_ragged(w.seed, wl.K, [0] * B, ends, hkv, 128)
+    v = wl.normal_tokens_ragged(w.seed, wl.V, [0] * B, ends, hkv, 128)
+    q = wl.normal_tokens(w.seed + 1, wl.Q, B, 0, T, hq, 128)
+    cache = lib.KVCache(layer, B, w.len_hi, zero=False)
+    for b in range(B):
+        for p0 in range(0, past[b], 32768):
+            n = min(32768, past[b] - p0)
+            lib.kv_append(layer, cache, dev(k[b][None, p0:p0 + n]), dev(v[b][None, p0:p0 + n]),
+                          torch.tensor([p0], dtype=torch.int32, device="cuda"), max_end_pos=p0 + n, batch=1,
+                          batch_offset=b)
+    kn = np.stack([k[b][past[b]:past[b] + T] for b in range(B)])
+    vn = np.stack([v[b][past[b]:past[b] + T] for b in range(B)])
+    out = torch.empty((B, T, hq, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((B, T, hq), dtype=torch.float32, device="cuda")
+    ws = lib.decode_block_workspace(layer, B, T, w.len_hi)
+    lib.attn_decode_block(layer, cache, dev(q), dev(kn), dev(vn), torch.tensor(past, dtype=torch.int32, device="cuda"),
+                          w.len_hi, out, ws, lse=lse)
+    torch.cuda.synchronize()
+    check_block(layer, past, T, q, k, v, host_bits(out), lse.cpu().numpy(), f"{w.name} T={T}")

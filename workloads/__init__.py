@@ -132,19 +132,29 @@ def normal_tokens(seed: int, tensor: int, batch: int, pos0: int, ntok: int, head
     return out
 
 
-def normal_tokens_ragged(seed: int, tensor: int, starts, counts, heads: int, d: int) -> list:
+def normal_tokens_ragged(seed: int, tensor: int, starts, counts, heads: int, d: int,
+                         threads: int | None = None) -> list:
     """Per batch row b: bf16 bits [counts[b], heads, d] for positions
     [starts[b], starts[b] + counts[b]); identical values to normal_tokens."""
-    res = []
-    for b, (s, c) in enumerate(zip(starts, counts)):
-        blk0, blk1 = s // BLOCK_TOKENS, (s + c - 1) // BLOCK_TOKENS
-        arr = np.empty((c, heads, d), dtype=np.uint16)
-        for blk in range(blk0, blk1 + 1) if c > 0 else []:
-            g = _block_rng(seed, tensor, b, blk)
-            vals = g.standard_normal((BLOCK_TOKENS, heads, d), dtype=np.float32)
-            lo, hi = max(s, blk * BLOCK_TOKENS), min(s + c, (blk + 1) * BLOCK_TOKENS)
-            arr[lo - s:hi - s] = f32_to_bf16_bits(vals[lo - blk * BLOCK_TOKENS:hi - blk * BLOCK_TOKENS])
-        res.append(arr)
+    res = [np.empty((c, heads, d), dtype=np.uint16) for c in counts]
+    jobs = [(b, blk) for b, (s, c) in enumerate(zip(starts, counts)) if c > 0
+            for blk in range(s // BLOCK_TOKENS, (s + c - 1) // BLOCK_TOKENS + 1)]
+
+    def run(job):
+        b, blk = job
+        s, c = starts[b], counts[b]
+        g = _block_rng(seed, tensor, b, blk)
+        vals = g.standard_normal((BLOCK_TOKENS, heads, d), dtype=np.float32)
+        lo, hi = max(s, blk * BLOCK_TOKENS), min(s + c, (blk + 1) * BLOCK_TOKENS)
+        res[b][lo - s:hi - s] = f32_to_bf16_bits(vals[lo - blk * BLOCK_TOKENS:hi - blk * BLOCK_TOKENS])
+
+    nt = threads or _threads()
+    if nt == 1 or len(jobs) <= 1:
+        for j in jobs:
+            run(j)
+    else:
+        with ThreadPoolExecutor(nt) as ex:
+            list(ex.map(run, jobs))
     return res
 
 
