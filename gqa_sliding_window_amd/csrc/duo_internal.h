@@ -151,11 +151,13 @@ struct PrefillItem {
 };
 
 // Workgroup -> work item. Units (one kPrefillRows-row query tile of one KV-head group)
-// are ordered heaviest first: main-class units before streaming units, later
-// query tiles before earlier ones. Unit u runs on XCD u % 8 (workgroups are
-// dispatched to XCDs round-robin), so every XCD gets an equal share of each
-// cost level; the `group` query heads of one unit are consecutive on that XCD
-// and share the unit's K/V tiles through its L2.
+// are ordered main-class units before streaming units. Unit u runs on XCD
+// u % 8 (workgroups are dispatched to XCDs round-robin); the `group` query
+// heads of one unit are consecutive on that XCD and share the unit's K/V
+// tiles through its L2. When a class's (batch, KV head) groups fill whole
+// 8-wide stripes, each XCD takes its groups one at a time, later query tiles
+// first; otherwise all groups advance together, later query tiles first, so
+// every XCD gets an equal share of each cost level.
 // (32-bit arithmetic: the host keeps grids below 2^31 workgroups; a 64-bit
 // division would run as a long software sequence in every workgroup.)
 __host__ __device__ inline PrefillItem prefill_item(const PrefillParams& p, int block) {
@@ -171,8 +173,19 @@ __host__ __device__ inline PrefillItem prefill_item(const PrefillParams& p, int 
   it.cls = kMain;
   if (u >= p.n_units_main) { u -= p.n_units_main; it.cls = kStream; n_class = p.n_stream; }
   const int groups = p.batch * n_class;
-  it.qtile = p.n_qtiles - 1 - u / groups;
-  const int grp = u % groups;
+  int grp;
+  if (groups % kXcds == 0) {
+    // Whole stripes: XCD x = u % 8 walks its own KV groups x, x + 8, ... one
+    // after another, each from its last query tile to its first, so the
+    // query tiles that share a group's K/V prefix run together in that XCD's
+    // L2 (interleaving the groups would need all of them in one L2).
+    const int j = u / kXcds;
+    grp = (j / p.n_qtiles) * kXcds + u % kXcds;
+    it.qtile = p.n_qtiles - 1 - j % p.n_qtiles;
+  } else {
+    it.qtile = p.n_qtiles - 1 - u / groups;
+    grp = u % groups;
+  }
   it.b = grp / n_class;
   it.rank = grp % n_class;
   it.kvh = class_head(p.stream_mask, p.hkv, it.cls, it.rank);

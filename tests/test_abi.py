@@ -160,6 +160,7 @@ def _expected_tiles(layer, qa, qb, streaming):
 
 @pytest.mark.parametrize("case", [
     dict(layer=Layer(), B=2, T=1000, P=0),
+    dict(layer=Layer(num_q_heads=12, num_kv_heads=2), B=1, T=1000, P=0),
     dict(layer=Layer(kind=SLIDING, window=512, num_q_heads=12, num_kv_heads=2), B=1, T=1024, P=0),
     dict(layer=Layer(full_attention_heads=[0, 0, 0, 0, 1, 0, 1, 0]), B=1, T=8192, P=16384),
     dict(layer=Layer(full_attention_heads=[0] * 8), B=3, T=77, P=5),
@@ -179,12 +180,27 @@ def test_prefill_plan_covers_every_tile_once_and_skips_masked(lib, case):
         qb = min(qa + rows - 1, P + T - 1)
         streaming = mask is not None and mask[h // G] == 0
         assert nt == _expected_tiles(L, qa, qb, streaming)
-    # heaviest-first per XCD: along each XCD's sequence the key-tile count never increases
-    # within the main class
+    # XCD order (workgroup i runs on XCD i % 8). With whole 8-wide stripes of
+    # (batch, KV head) groups, each XCD walks its own groups one at a time
+    # (every unit of a group on one XCD, one contiguous run per group),
+    # heaviest query tile first within the run. Otherwise all groups advance
+    # together, and for a full layer the tile count never increases along an
+    # XCD's sequence.
+    groups_main = B * (L.num_kv_heads if mask is None else sum(1 for m in mask if m))
+    xcd_of_group = {}
     for x in range(8):
-        seq = [int(r[3]) for r in items[x::8] if r[0] >= 0]
-        if mask is None and L.kind == FULL:
-            assert all(a >= b for a, b in zip(seq, seq[1:]))
+        seq = [r for r in items[x::8] if r[0] >= 0]
+        if mask is None and L.kind == FULL and groups_main % 8 == 0:
+            keys = [(int(r[0]), int(r[1]) // G) for r in seq]
+            runs = [k for i, k in enumerate(keys) if i == 0 or keys[i - 1] != k]
+            assert len(runs) == len(set(runs)), "a group's units are not contiguous on its XCD"
+            for k in set(keys):
+                assert xcd_of_group.setdefault(k, x) == x, "a group spans two XCDs"
+                nts = [int(r[3]) for r, kk in zip(seq, keys) if kk == k]
+                assert all(a >= b for a, b in zip(nts, nts[1:]))
+        elif mask is None and L.kind == FULL:
+            nts = [int(r[3]) for r in seq]
+            assert all(a >= b for a, b in zip(nts, nts[1:]))
 
 
 def test_decode_plan(lib):
