@@ -1,0 +1,64 @@
+/* Plain C99 client of duo_attn.h: the header compiles as C and the host-only
+ * entry points behave as documented (no GPU is touched). Exit status 0 on
+ * success; prints the first failed check otherwise. */
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "duo_attn.h"
+
+#define CHECK(c) do { if (!(c)) { printf("check failed at line %d: %s (%s)\n", __LINE__, #c, duo_last_error()); return 1; } } while (0)
+
+int main(void) {
+  const uint8_t mask[8] = {0, 1, 0, 0, 1, 0, 0, 0};
+  duo_layer L;
+  memset(&L, 0, sizeof L);
+  L.num_q_heads = 48; L.num_kv_heads = 8; L.head_dim = 128; L.kind = DUO_LAYER_FULL;
+  L.window = 0; L.sink = 64; L.recent = 256; L.full_attention_heads = mask; L.scale = 0.f;
+
+  CHECK(duo_attn_version() == DUO_ATTN_VERSION);
+  CHECK(duo_prefill_tile_rows() > 0);
+
+  /* head plan: full heads 1 and 4 ranked 0, 1; the rest streaming, ranked in order */
+  int32_t cls[8], rank[8], nm = -1, ns = -1;
+  CHECK(duo_head_plan(&L, cls, rank, &nm, &ns) == DUO_OK);
+  CHECK(nm == 2 && ns == 6);
+  CHECK(cls[1] == 0 && rank[1] == 0 && cls[4] == 0 && rank[4] == 1);
+  CHECK(cls[0] == 1 && rank[0] == 0 && cls[7] == 1 && rank[7] == 5);
+
+  /* static cache bytes: one of k/v per class */
+  int64_t mb = 0, sb = 0;
+  CHECK(duo_kv_cache_bytes(&L, 2, 1000, &mb, &sb) == DUO_OK);
+  CHECK(mb == (int64_t)2 * 2 * 1000 * 128 * 2);
+  CHECK(sb == (int64_t)2 * 6 * (64 + 256) * 128 * 2);
+
+  /* cache report for lengths 10 and 5000 */
+  const int32_t lens[2] = {10, 5000};
+  duo_cache_report rep;
+  CHECK(duo_kv_cache_report(&L, 2, 5000, lens, &rep) == DUO_OK);
+  CHECK(rep.main_active == 2 * (10 + 5000));
+  CHECK(rep.stream_active == 6 * (10 + 320));
+  CHECK(rep.base_active == 8 * (10 + 5000));
+
+  /* rotary frequencies: plain RoPE theta 10000 */
+  duo_rope r = {10000.f, 1.f, 0, 0.f, 0.f, 1.f};
+  double f[64];
+  CHECK(duo_rope_frequencies(&r, f) == DUO_OK);
+  CHECK(f[0] == 1.0 && fabs(f[1] - pow(10000.0, -2.0 / 128)) < 1e-15);
+
+  /* validation errors leave nothing launched and set a message */
+  duo_layer bad = L;
+  bad.head_dim = 64;
+  CHECK(duo_head_plan(&bad, cls, rank, &nm, &ns) == DUO_ERR_UNSUPPORTED);
+  CHECK(strlen(duo_last_error()) > 0);
+  CHECK(duo_attn_decode_workspace_bytes(&bad, 4, 1000) == 0);
+  CHECK(duo_attn_decode_workspace_bytes(&L, 4, 1000) > 0);
+  CHECK(duo_attn_decode_block_workspace_bytes(&L, 4, 65, 1000) == 0); /* more than 64 tokens */
+  r.theta = 1.f;
+  CHECK(duo_rope_frequencies(&r, f) == DUO_ERR_INVALID_ARG);
+
+  /* empty calls are no-ops */
+  CHECK(duo_attn_prefill(&L, NULL, 0, NULL, NULL, NULL, 0, 0, NULL, NULL, NULL, NULL, NULL) == DUO_OK);
+  printf("ok\n");
+  return 0;
+}
