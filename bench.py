@@ -345,9 +345,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sections", default="prefill,prologue,decode,chunked",
-                    help="comma list of prefill, prologue (needs prefill), decode, chunked, copy "
-                         "(copy = counter calibration: a plain 1 GiB device copy)")
+    ap.add_argument("--sections", default="prefill,sliding,prologue,decode,chunked",
+                    help="comma list of prefill, sliding and prologue (both need prefill), decode, chunked, "
+                         "copy (copy = counter calibration: a plain 1 GiB device copy)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 = skip)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -369,7 +369,7 @@ def main():
            "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16)"}
 
-    w2 = qkv = None
+    w2 = qkv = devs = None
     if "prefill" in sections:
         w2, qkv, flops, ms, devs = bench_prefill(torch, G, wl, timer, args.warmup, args.steps)
         tflops = flops / (ms * 1e-3) / 1e12
@@ -390,10 +390,22 @@ def main():
                            "frac": tflops / PEAK_MFMA_BF16_TFLOPS, "traffic": traffic,
                            "frac_of_measured_ceiling": tflops / MEASURED_MFMA_BF16_TFLOPS}
         log(f"prefill: {ms:.3f} ms/step, {tflops:.1f} TFLOP/s")
-        if "prologue" in sections:
-            res["prologue_epilogue"] = bench_prologue_epilogue(torch, G, wl, timer, args.warmup, args.steps, w2,
-                                                               flops, ms, devs)
-        del devs
+    if "sliding" in sections and devs is not None:
+        # the same shape on a 512-token sliding-window layer (30 of the model's
+        # 40 layers are of this kind)
+        layer_s = G.Layer(kind=G.SLIDING, window=512)
+        fl_s = G.prefill_flops(layer_s, w2.batch, w2.seq)
+        lq, qd_, kd_, vd_, od_ = devs
+        ms_s = timer.run(lambda i: G.attn_prefill(layer_s, qd_, kd_, vd_, od_), args.warmup, args.steps)
+        res["sliding_prefill"] = {"workload": w2.name + " on a sliding-window layer (w 512)",
+                                  "algorithmic_flop": fl_s, "ms": ms_s,
+                                  "TFLOP/s": fl_s / (ms_s * 1e-3) / 1e12,
+                                  "ms_median": timer.last["median_ms"], "ms_min": timer.last["min_ms"]}
+        log(f"sliding prefill: {ms_s:.3f} ms, {res['sliding_prefill']['TFLOP/s']:.1f} TFLOP/s")
+    if "prologue" in sections and devs is not None:
+        res["prologue_epilogue"] = bench_prologue_epilogue(torch, G, wl, timer, args.warmup, args.steps, w2,
+                                                           flops, ms, devs)
+    devs = None
 
     if "decode" in sections:
         d = {}

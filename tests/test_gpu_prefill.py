@@ -180,6 +180,19 @@ def test_full_prefill_workload_sampled(lib):
     compare_rows(layer, q, k, v, out, lse, rows, w.name)
 
 
+def test_sliding_prefill_headline_shape_sampled(lib):
+    """The headline shape (batch 4, 48/8 heads, 8192 tokens) on a 512-token
+    sliding-window layer, the layer kind bench.py times beside the full one;
+    2048 seeded rows including the window edges."""
+    w = wl.WORKLOADS[2]
+    announce(f"prefill parity {w.name} sliding w512")
+    layer = lib.Layer(kind=lib.SLIDING, window=512)
+    q, k, v = _gen(w.seed, w.batch, w.seq, w.hq, w.hkv)
+    out, lse = run_chunked(lib, layer, q, k, v, w.seq)
+    rows = wl.sample_query_rows(w, w.seq, 2048, must=(0, 511, 512, 513, 1023, 1024, 8191))
+    compare_rows(layer, q, k, v, out, lse, rows, w.name + " sliding w512")
+
+
 def test_duo_chunked_prefill_workload_sampled(lib):
     """DuoAttention long-context chunked prefill at full size: batch 1, 131072
     tokens in 16 chunks of 8192 (attend, then append), 48/8 heads, the seeded
