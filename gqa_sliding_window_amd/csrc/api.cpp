@@ -30,7 +30,10 @@ int ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-constexpr int64_t kMaxPos = 0x7FFFFFFF;   // positions are int32 on the device side
+// Positions are int32 on the device side; the kernels form tile and row
+// bounds up to a few hundred past the last position (a 256-row query tile,
+// 64-key tiles), so the limit keeps a margin below 2^31.
+constexpr int64_t kMaxPos = 0x7FFFFFFF - 1024;
 constexpr int64_t kMaxGrid = 0x7FFFFFFF;  // workgroups per launch
 constexpr int32_t kMaxBlockTokens = 64;   // query tokens per sequence of a block decode
 
@@ -402,7 +405,7 @@ int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens, 
   int rc = check_layer(layer, &L);
   if (rc) return rc;
   if (batch < 0 || num_tokens < 0 || start_pos < 0) return fail(DUO_ERR_INVALID_ARG, "negative size");
-  if (start_pos + num_tokens > kMaxPos) return fail(DUO_ERR_INVALID_ARG, "positions exceed int32");
+  if (start_pos + num_tokens > kMaxPos) return fail(DUO_ERR_INVALID_ARG, "positions exceed %lld", (long long)kMaxPos);
   PrefillParams p;
   int64_t nb = 0;
   if (batch > 0 && num_tokens > 0 && (rc = build_prefill(L, batch, num_tokens, start_pos, &p, &nb))) return rc;
@@ -432,7 +435,7 @@ int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t b
   int rc = check_layer(layer, &L);
   if (rc) return rc;
   if (batch < 0 || num_tokens < 0 || start_pos < 0) return fail(DUO_ERR_INVALID_ARG, "negative size or start_pos");
-  if (start_pos + num_tokens > kMaxPos) return fail(DUO_ERR_INVALID_ARG, "positions exceed int32");
+  if (start_pos + num_tokens > kMaxPos) return fail(DUO_ERR_INVALID_ARG, "positions exceed %lld", (long long)kMaxPos);
   if (batch == 0 || num_tokens == 0) return ok();
   if (q == nullptr || k == nullptr || v == nullptr || out == nullptr)
     return fail(DUO_ERR_INVALID_ARG, "q, k, v and out must not be NULL");

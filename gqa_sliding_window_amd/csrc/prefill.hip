@@ -16,9 +16,10 @@
 // outside the ranges are never visited and only tiles on a range edge, the
 // diagonal or a band edge evaluate the per-element predicate. Keys before
 // start_pos are read from the cache (slot per class), the chunk's own keys
-// from the k/v inputs. Positions are 32-bit (the host bounds them below 2^31);
-// a tile that lies wholly in the chunk or in a contiguous stretch of the cache
-// is addressed from one base pointer, other tiles row by row.
+// from the k/v inputs. Positions are 32-bit (the host keeps them 1024 below
+// 2^31, so tile and row bounds formed past the last position cannot
+// overflow); a tile that lies wholly in the chunk or in a contiguous stretch
+// of the cache is addressed from one base pointer, other tiles row by row.
 #include "duo_internal.h"
 #include "mfma_common.h"
 #include "qk_prologue.h"

@@ -44,6 +44,10 @@
  *    means nothing was launched. duo_last_error() then describes the problem
  *    (thread-local, valid until the next call on the same thread).
  *  - Calls on different streams that write the same cache or workspace race.
+ *  - Positions (start_pos + num_tokens, max_seq_len, max_end_pos,
+ *    max_past_len + num_tokens) must stay at or below 2^31 - 1025
+ *    (INVALID_ARG otherwise): the kernels use 32-bit positions and form tile
+ *    bounds a little past the last one.
  */
 #ifndef DUO_ATTN_H
 #define DUO_ATTN_H
@@ -292,7 +296,8 @@ int duo_rope_frequencies(const duo_rope* rope, double* freqs);
  * appended (attend, then append; append it afterwards without a prologue).
  * x, y      : device bf16 [batch, num_tokens, heads, 128], 16-byte aligned;
  *             y == x works in place, other overlaps are undefined.
- * start_pos : device int32 [batch].
+ * start_pos : device int32 [batch]; start_pos[b] + num_tokens must respect
+ *             the position limit above (device data: not checked).
  * heads     : 1 .. 4096. One HBM pass over x and y. */
 int duo_qk_prologue(const duo_prologue* prologue, int32_t batch, int32_t num_tokens, int32_t heads,
                     const void* x, void* y, const int32_t* start_pos, void* stream);

@@ -291,3 +291,22 @@ def test_rope_frequencies_match_the_oracle(lib, rope):
                                    r.original_max_position, float(np.float32(r.beta_fast)),
                                    float(np.float32(r.beta_slow)))
     assert np.allclose(got, want, rtol=1e-13, atol=0)
+
+
+def test_position_limit(lib):
+    """Positions stay 1024 below 2^31 (32-bit device positions with tile
+    bounds formed past the last one)."""
+    top = (1 << 31) - 1 - 1024
+    q = FakeTensor((1, 8, 48, 128))
+    kv = FakeTensor((1, 8, 8, 128))
+    L = Layer(kind=SLIDING, window=512)
+    ring = FakeCache(cap=512)
+    # the last allowed chunk (start_pos + num_tokens = top) passes the position
+    # check and is refused only for its misaligned lse, so nothing launches
+    assert _err(g.attn_prefill, L, q, kv, kv, q, start_pos=top - 8, past=ring, stream=0, lse=FakeTensor((1,), 2)) == -1
+    assert "lse" in lib.load().duo_last_error().decode()
+    assert _err(g.attn_prefill, L, q, kv, kv, q, start_pos=top - 7, past=ring, stream=0) == -1
+    assert "positions exceed" in lib.load().duo_last_error().decode()
+    assert _err(g.kv_append, L, ring, kv, kv, FakeTensor((1,)), max_end_pos=top + 1, stream=0) == -1
+    assert g.decode_workspace_bytes(L, 4, top) > 0
+    assert g.decode_workspace_bytes(L, 4, top + 1) == 0
