@@ -307,6 +307,9 @@ def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for f in ("prefill.hip", "duo_internal.h", "mfma_common.h", "qk_prologue.h"):
         h.update(open(os.path.join(HERE, "gqa_sliding_window_amd", "csrc", f), "rb").read())
+    from gqa_sliding_window_amd import build as B
+    flags = [f for f in B.common_flags() + B.SOURCE_FLAGS.get("prefill.hip", []) if not f.startswith("-I")]
+    h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 

@@ -2,7 +2,10 @@
 
 Each source is compiled to an object in parallel, then linked into a shared
 library next to this file. Packed-fp32 VALU instructions are disabled for all
-device code.
+device code. The prefill is compiled without NaN semantics: its row maxima
+then fold into three-operand max instructions (about 2% faster measured);
+infinities, which its masking uses, keep their meaning. A NaN in its inputs
+gives an unspecified output.
 """
 from __future__ import annotations
 
@@ -20,6 +23,8 @@ LIB_NAME = "libduoattn.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 SOURCES = ["api.cpp", "kv_append.hip", "prefill.hip", "decode.hip"]
 ARCH = "gfx950"
+# flags for one source only
+SOURCE_FLAGS = {"prefill.hip": ["-fno-honor-nans"]}
 
 
 def hipcc() -> str:
@@ -43,7 +48,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *common_flags(), *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *common_flags(), *SOURCE_FLAGS.get(src, []), *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj]
         if src.endswith(".cpp"):
             cmd[1:1] = ["-x", "hip"]
         r = subprocess.run(cmd, capture_output=True, text=True)

@@ -48,6 +48,8 @@
  *    max_past_len + num_tokens) must stay at or below 2^31 - 1025
  *    (INVALID_ARG otherwise): the kernels use 32-bit positions and form tile
  *    bounds a little past the last one.
+ *  - Inputs are finite numbers. The prefill is built without NaN semantics,
+ *    so a NaN in its inputs gives unspecified (but in-bounds) results.
  */
 #ifndef DUO_ATTN_H
 #define DUO_ATTN_H
