@@ -185,6 +185,54 @@ def _ptr(t) -> int:
     return t.data_ptr()
 
 
+def _need(t, name: str, shape, dtype: str):
+    """Reject a tensor that the kernels would misread: wrong dtype or shape
+    (None in `shape` matches any extent) or not densely packed (its device
+    is checked by _need_device). The C ABI takes bare pointers and cannot check these.
+    Anything that is not a torch tensor (a raw address, an object with a
+    data_ptr) passes unchecked."""
+    import torch
+    if not isinstance(t, torch.Tensor):
+        return
+    want = getattr(torch, dtype)
+    if t.dtype != want:
+        raise ValueError(f"{name}: dtype {t.dtype}, expected {want}")
+    if shape is not None:
+        got = tuple(t.shape)
+        if len(got) != len(shape) or any(w is not None and g != w for g, w in zip(got, shape)):
+            exp = tuple("*" if w is None else w for w in shape)
+            raise ValueError(f"{name}: shape {got}, expected {exp}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_device(**tensors):
+    """Every torch tensor given is in device memory (checked after the
+    dtype and shape checks of all arguments)."""
+    import torch
+    for name, t in tensors.items():
+        if isinstance(t, torch.Tensor) and not t.is_cuda:
+            raise ValueError(f"{name} must be in device memory")
+
+
+def _need_batch(t, name: str, batch: int):
+    """t's leading extent covers `batch` sequences."""
+    import torch
+    if isinstance(t, torch.Tensor) and t.shape[0] < batch:
+        raise ValueError(f"{name}: leading extent {t.shape[0]} < batch {batch}")
+
+
+def _need_cache(cache, batch: int, batch_offset: int = 0):
+    if isinstance(cache, KVCache) and (batch_offset < 0 or batch_offset + batch > cache.batch):
+        raise ValueError(f"cache holds {cache.batch} sequences; the call uses [{batch_offset}, {batch_offset + batch})")
+
+
+def _need_prologue(pro, name: str):
+    if pro is not None:
+        _need(pro.norm_weight, f"{name}.norm_weight", (HEAD_DIM,), "float32")
+        _need_device(**{f"{name}.norm_weight": pro.norm_weight})
+
+
 def _stream(stream) -> int:
     if stream is not None:
         return stream if isinstance(stream, int) else stream.cuda_stream
@@ -222,9 +270,18 @@ def kv_append(layer: Layer, cache: KVCache, k_new, v_new, start_pos, max_end_pos
               k_prologue: Optional[Prologue] = None):
     """duo_kv_append: k_new/v_new [B, T, Hkv, 128] bf16, start_pos int32 [B]
     (device); k_prologue transforms K on its way into the cache."""
-    lib = load()
     B = k_new.shape[0] if batch is None else batch
     T = k_new.shape[1]
+    hkv = layer.num_kv_heads
+    _need(k_new, "k_new", (None, T, hkv, HEAD_DIM), "bfloat16")
+    _need(v_new, "v_new", (None, T, hkv, HEAD_DIM), "bfloat16")
+    _need(start_pos, "start_pos", (None,), "int32")
+    for t, n in ((k_new, "k_new"), (v_new, "v_new"), (start_pos, "start_pos")):
+        _need_batch(t, n, B)
+    _need_cache(cache, B, batch_offset)
+    _need_prologue(k_prologue, "k_prologue")
+    _need_device(k_new=k_new, v_new=v_new, start_pos=start_pos)
+    lib = load()
     cl, cc = layer._c(), cache._c(batch_offset)
     _check(lib.duo_kv_append(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(k_new), _ptr(v_new), T,
                              _ptr(start_pos), int(max_end_pos), _prologue(k_prologue), _stream(stream)))
@@ -245,6 +302,11 @@ def qk_prologue(prologue: Prologue, x, start_pos, y=None, stream=None):
     y is None. Returns y."""
     y = x if y is None else y
     B, T, H = x.shape[0], x.shape[1], x.shape[2]
+    _need(x, "x", (B, T, H, HEAD_DIM), "bfloat16")
+    _need(y, "y", (B, T, H, HEAD_DIM), "bfloat16")
+    _need(start_pos, "start_pos", (B,), "int32")
+    _need_prologue(prologue, "prologue")
+    _need_device(x=x, y=y, start_pos=start_pos)
     _check(load().duo_qk_prologue(_prologue(prologue), B, T, H, _ptr(x), _ptr(y), _ptr(start_pos),
                                   _stream(stream)))
     return y
@@ -256,8 +318,11 @@ def _epilogue(out, sink_logits, gate):
     without its last dimension (one value per row and head)."""
     if sink_logits is None and gate is None:
         return None
+    hq = out.shape[-2]
+    _need(sink_logits, "sink_logits", (hq,), "float32")
     mode = GATE_NONE
     if gate is not None:
+        _need(gate, "gate", None, "bfloat16")
         if tuple(gate.shape) == tuple(out.shape):
             mode = GATE_PER_ELEMENT
         elif tuple(gate.shape) == tuple(out.shape[:-1]):
@@ -265,6 +330,7 @@ def _epilogue(out, sink_logits, gate):
         else:
             raise ValueError(f"gate shape {tuple(gate.shape)} matches neither {tuple(out.shape)} "
                              f"nor {tuple(out.shape[:-1])}")
+    _need_device(sink_logits=sink_logits, gate=gate)
     return ctypes.byref(_Epilogue(_ptr(sink_logits), _ptr(gate), mode))
 
 
@@ -272,13 +338,24 @@ def attn_prefill(layer: Layer, q, k, v, out, start_pos: int = 0, past: Optional[
                  lse=None, stream=None, sink_logits=None, gate=None, q_prologue: Optional[Prologue] = None):
     """duo_attn_prefill: q [B, T, Hq, 128], k/v [B, T, Hkv, 128], out like q;
     optional attention-sink logits and output gate (see _epilogue)."""
-    lib = load()
     B, T = q.shape[0], q.shape[1]
+    hq, hkv = layer.num_q_heads, layer.num_kv_heads
+    _need(q, "q", (B, T, hq, HEAD_DIM), "bfloat16")
+    _need(k, "k", (B, T, hkv, HEAD_DIM), "bfloat16")
+    _need(v, "v", (B, T, hkv, HEAD_DIM), "bfloat16")
+    _need(out, "out", (B, T, hq, HEAD_DIM), "bfloat16")
+    _need(lse, "lse", (B, hq, T), "float32")
+    _need_prologue(q_prologue, "q_prologue")
+    if past is not None:
+        _need_cache(past, B)
+    epi = _epilogue(out, sink_logits, gate)
+    _need_device(q=q, k=k, v=v, out=out, lse=lse)
+    lib = load()
     cl = layer._c()
     cc = past._c() if past is not None else None
     _check(lib.duo_attn_prefill(ctypes.byref(cl), ctypes.byref(cc) if cc is not None else None, B,
                                 _ptr(q), _ptr(k), _ptr(v), T, int(start_pos), _ptr(out), _ptr(lse),
-                                _prologue(q_prologue), _epilogue(out, sink_logits, gate), _stream(stream)))
+                                _prologue(q_prologue), epi, _stream(stream)))
 
 
 def decode_workspace_bytes(layer: Layer, batch: int, max_seq_len: int) -> int:
@@ -304,13 +381,23 @@ def init_decode_workspace(ws, stream=None):
 def attn_decode(layer: Layer, cache: KVCache, q, seq_lens, max_seq_len: int, out, workspace,
                 lse=None, stream=None, sink_logits=None, gate=None, q_prologue: Optional[Prologue] = None):
     """duo_attn_decode: q [B, Hq, 128], seq_lens int32 [B] (device), out like q."""
-    lib = load()
     B = q.shape[0]
+    hq = layer.num_q_heads
+    _need(q, "q", (B, hq, HEAD_DIM), "bfloat16")
+    _need(seq_lens, "seq_lens", (B,), "int32")
+    _need(out, "out", (B, hq, HEAD_DIM), "bfloat16")
+    _need(lse, "lse", (B, hq), "float32")
+    _need(workspace, "workspace", None, "float32")
+    _need_prologue(q_prologue, "q_prologue")
+    _need_cache(cache, B)
+    epi = _epilogue(out, sink_logits, gate)
+    _need_device(q=q, seq_lens=seq_lens, out=out, lse=lse, workspace=workspace)
+    lib = load()
     cl, cc = layer._c(), cache._c()
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib.duo_attn_decode(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(q), _ptr(seq_lens),
                                int(max_seq_len), _ptr(out), _ptr(lse), _ptr(workspace), nbytes,
-                               _prologue(q_prologue), _epilogue(out, sink_logits, gate), _stream(stream)))
+                               _prologue(q_prologue), epi, _stream(stream)))
 
 
 def decode_block_workspace_bytes(layer: Layer, batch: int, num_tokens: int, max_past_len: int) -> int:
@@ -333,14 +420,26 @@ def attn_decode_block(layer: Layer, cache: KVCache, q, k_new, v_new, past_lens, 
                       q_prologue: Optional[Prologue] = None):
     """duo_attn_decode_block: q/out [B, T, Hq, 128], k_new/v_new [B, T, Hkv, 128],
     past_lens int32 [B] (device): cached positions before the block."""
-    lib = load()
     B, T = q.shape[0], q.shape[1]
+    hq, hkv = layer.num_q_heads, layer.num_kv_heads
+    _need(q, "q", (B, T, hq, HEAD_DIM), "bfloat16")
+    _need(k_new, "k_new", (B, T, hkv, HEAD_DIM), "bfloat16")
+    _need(v_new, "v_new", (B, T, hkv, HEAD_DIM), "bfloat16")
+    _need(past_lens, "past_lens", (B,), "int32")
+    _need(out, "out", (B, T, hq, HEAD_DIM), "bfloat16")
+    _need(lse, "lse", (B, T, hq), "float32")
+    _need(workspace, "workspace", None, "float32")
+    _need_prologue(q_prologue, "q_prologue")
+    _need_cache(cache, B)
+    epi = _epilogue(out, sink_logits, gate)
+    _need_device(q=q, k_new=k_new, v_new=v_new, past_lens=past_lens, out=out, lse=lse, workspace=workspace)
+    lib = load()
     cl, cc = layer._c(), cache._c()
     nbytes = workspace.numel() * workspace.element_size()
     _check(lib.duo_attn_decode_block(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(q), _ptr(k_new), _ptr(v_new),
                                      T, _ptr(past_lens), int(max_past_len), _ptr(out), _ptr(lse),
                                      _ptr(workspace), nbytes, _prologue(q_prologue),
-                                     _epilogue(out, sink_logits, gate), _stream(stream)))
+                                     epi, _stream(stream)))
 
 
 def head_plan(layer: Layer):

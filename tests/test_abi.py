@@ -310,3 +310,33 @@ def test_position_limit(lib):
     assert _err(g.kv_append, L, ring, kv, kv, FakeTensor((1,)), max_end_pos=top + 1, stream=0) == -1
     assert g.decode_workspace_bytes(L, 4, top) > 0
     assert g.decode_workspace_bytes(L, 4, top + 1) == 0
+
+
+def test_binding_rejects_misshaped_tensors():
+    """The binding checks dtype, shape, packing and device of torch tensors
+    before any call: the C ABI sees bare pointers and could not."""
+    import torch
+    L = Layer()
+    q = torch.zeros(1, 8, 48, 128, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 8, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="dtype"):
+        g.attn_prefill(L, q.float(), kv, kv, q, stream=0)
+    with pytest.raises(ValueError, match="shape"):
+        g.attn_prefill(L, q, torch.zeros(1, 8, 4, 128, dtype=torch.bfloat16), kv, q, stream=0)
+    with pytest.raises(ValueError, match="shape"):
+        g.attn_prefill(L, q, kv, kv, q, lse=torch.zeros(1, 8, 48), stream=0)
+    with pytest.raises(ValueError, match="contiguous"):
+        g.attn_prefill(L, q, kv, kv, q.transpose(1, 2).contiguous().transpose(1, 2), stream=0)
+    with pytest.raises(ValueError, match="device memory"):
+        g.attn_prefill(L, q, kv, kv, q, stream=0)
+    with pytest.raises(ValueError, match="sink_logits"):
+        g.attn_prefill(L, q, kv, kv, q, sink_logits=torch.zeros(8), stream=0)
+    qd = torch.zeros(2, 48, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="seq_lens"):
+        g.attn_decode(L, FakeCache(), qd, torch.zeros(2, dtype=torch.int64), 16, qd, FakeTensor((64,)), stream=0)
+    with pytest.raises(ValueError, match="start_pos"):
+        g.kv_append(L, FakeCache(), kv, kv, torch.zeros(1, dtype=torch.int64), max_end_pos=16, stream=0)
+    with pytest.raises(ValueError, match="leading extent"):
+        g.kv_append(L, FakeCache(), kv, kv, torch.zeros(0, dtype=torch.int32), max_end_pos=16, stream=0)
+    with pytest.raises(ValueError, match="norm_weight"):
+        g.qk_prologue(g.Prologue(norm_weight=torch.zeros(64)), q, torch.zeros(1, dtype=torch.int32))
