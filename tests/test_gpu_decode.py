@@ -174,3 +174,23 @@ def test_decode_equals_prefill_last_row(lib):
     pre = bits_to_f64(host_bits(out)[0, N - 1])
     d = np.abs(bits_to_f64(od[0]) - pre).max()
     assert d <= 1.6e-2, d
+
+
+def test_cache_offsets_past_2pow31_elements(lib):
+    """A full-layer cache of 16 x 8 x 131136 x 128 elements per K and per V,
+    more than 2^31. The last sequence fills 131072 positions, so the rows of
+    its last KV head from slot ~123000 on lie past element 2^31 (and every
+    row of sequences 8-15 past byte 2^31). Append and decode index the cache
+    with 64-bit offsets: every row of the long sequence and of the short
+    ones against the oracle."""
+    announce("cache with offsets past 2^31 elements: B16 cap 131136, 48/8")
+    layer = lib.Layer()
+    B, cap = 16, 131072 + 64
+    assert B * layer.num_kv_heads * cap * 128 > 2 ** 31
+    lengths = [100] + [1 + 7 * b for b in range(1, 15)] + [131072]
+    seqs = Seqs(2031, lengths, [0] * B, layer.num_kv_heads)
+    cache = lib.KVCache(layer, B, cap)
+    fill_cache(lib, layer, cache, seqs)
+    q = wl.decode_queries(2031, B, layer.num_q_heads, 128)
+    out, lse = run_decode(lib, layer, cache, q, lengths, max(lengths))
+    check_decode(layer, q, seqs, out, lse, "decode over a cache past 2^31 elements")
