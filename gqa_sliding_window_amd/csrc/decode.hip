@@ -522,7 +522,11 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   // Merge, 16 columns at a time: (max, sum) of every (column, split) into
   // LDS with all loads in flight, then per-column max / weights / normaliser,
   // then the weighted sum of the partial outputs (wave w takes splits w,
-  // w + kNW, ...; 4 splits per batch).
+  // w + kNW, ...; kBatch splits of loads in flight per wave). The merge runs
+  // in the launch's tail, so its latency is paid in full: the batch is as
+  // large as fits without spills (2 splits x 16 columns x 2 values in the
+  // single-token kernel; 1 in the block kernels, whose larger key loop
+  // leaves less room, where 4 spilled and serialised the loads).
   float* s_m = reinterpret_cast<float*>(smem);  // [16][kDecodeMaxSplits]
   float* s_w = s_m + 16 * kDecodeMaxSplits;       // [16][kDecodeMaxSplits] weights
   float* s_L = s_w + 16 * kDecodeMaxSplits;       // [16] output factors (1 / normaliser)
@@ -562,7 +566,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     float acc[kMaxGroup][2];
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) acc[h][0] = acc[h][1] = 0.f;
-    constexpr int kBatch = 4;
+    constexpr int kBatch = kBlock ? 1 : 2;
     for (int sp0 = wave; sp0 < n_used; sp0 += kNW * kBatch) {
       float v[kBatch][kMaxGroup][2];
 #pragma unroll
