@@ -202,12 +202,18 @@ __device__ __forceinline__ void coherent_store(float* p, float v) {
 __device__ __forceinline__ float coherent_load(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two consecutive floats (8-byte aligned) in one device-coherent load.
+__device__ __forceinline__ f32x2 coherent_load2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(f32x2, v);
+}
 
 // Output values (dim, dim + 1) of row bh: the unnormalised pair times the
 // row's normaliser and, if the call has one, the output gate.
 __device__ __forceinline__ void write_out_pair(const DecodeParams& p, int64_t bh, int dim, float a0, float a1,
                                                float inv) {
-  typedef float f32x2 __attribute__((ext_vector_type(2)));
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   float f0 = inv, f1 = inv;
   if (p.gate != nullptr) {
@@ -521,16 +527,13 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 
   // Merge, 16 columns at a time: (max, sum) of every (column, split) into
   // LDS with all loads in flight, then per-column max / weights / normaliser,
-  // then the weighted sum of the partial outputs (wave w takes splits w,
-  // w + kNW, ...; kBatch splits of loads in flight per wave). The merge runs
-  // in the launch's tail, so its latency is paid in full: the batch is as
-  // large as fits without spills (2 splits x 16 columns x 2 values in the
-  // single-token kernel; 1 in the block kernels, whose larger key loop
-  // leaves less room, where 4 spilled and serialised the loads).
+  // then the weighted sum of the partial outputs. The merge runs in the
+  // launch's tail (the other workgroups have finished), so its load latency
+  // is paid in full: each thread owns 4 dims of one column and keeps 8
+  // splits of loads in flight, with no cross-wave reduction.
   float* s_m = reinterpret_cast<float*>(smem);  // [16][kDecodeMaxSplits]
   float* s_w = s_m + 16 * kDecodeMaxSplits;       // [16][kDecodeMaxSplits] weights
   float* s_L = s_w + 16 * kDecodeMaxSplits;       // [16] output factors (1 / normaliser)
-  float* red = s_L + 16;                          // [kNW][16][128]
   for (int hb = 0; hb < n_half; ++hb) {
     const int c0 = 16 * hb;                       // first column of this half
     const int nc = min(16, n_cols - c0);
@@ -563,55 +566,37 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       }
     }
     __syncthreads();
-    float acc[kMaxGroup][2];
+    // weighted sum of the partial outputs: thread -> (column h, dims d..d+3),
+    // 32 threads per column, walking every split with kMergeU splits of
+    // 8-byte coherent loads in flight (past the last split the loads repeat
+    // it with weight 0, so they need no predicate)
+    constexpr int kMergeU = 8;
+    for (int e = tid; e < nc * 32; e += kThreads) {
+      const int h = e >> 5;
+      const int d = 4 * (e & 31);
+      const int64_t row = row_of(c0 + h);
+      const float* src = p.ws_acc + row * p.n_split_max * kD + d;
+      const float* wts = s_w + h * kDecodeMaxSplits;
+      float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+      for (int sp0 = 0; sp0 < n_used; sp0 += kMergeU) {
+        f32x2 lo[kMergeU], hi[kMergeU];
 #pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) acc[h][0] = acc[h][1] = 0.f;
-    constexpr int kBatch = kBlock ? 1 : 2;
-    for (int sp0 = wave; sp0 < n_used; sp0 += kNW * kBatch) {
-      float v[kBatch][kMaxGroup][2];
+        for (int u = 0; u < kMergeU; ++u) {
+          const float* q = src + (int64_t)min(sp0 + u, n_used - 1) * kD;
+          lo[u] = coherent_load2(q);
+          hi[u] = coherent_load2(q + 2);
+        }
 #pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int sp = sp0 + u * kNW;
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) {
-          if (h < nc && sp < n_used) {
-            const float* src = p.ws_acc + (row_of(c0 + h) * p.n_split_max + sp) * kD + 2 * lane;
-            v[u][h][0] = coherent_load(src);
-            v[u][h][1] = coherent_load(src + 1);
-          }
+        for (int u = 0; u < kMergeU; ++u) {
+          const float w = sp0 + u < n_used ? wts[sp0 + u] : 0.f;
+          a0 += w * lo[u].x;
+          a1 += w * lo[u].y;
+          a2 += w * hi[u].x;
+          a3 += w * hi[u].y;
         }
       }
-#pragma unroll
-      for (int u = 0; u < kBatch; ++u) {
-        const int sp = sp0 + u * kNW;
-#pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) {
-          if (h < nc && sp < n_used) {
-            const float w = s_w[h * kDecodeMaxSplits + sp];
-            acc[h][0] += w * v[u][h][0];
-            acc[h][1] += w * v[u][h][1];
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int h = 0; h < kMaxGroup; ++h) {
-      if (h < nc) {
-        red[(wave * 16 + h) * kD + 2 * lane] = acc[h][0];
-        red[(wave * 16 + h) * kD + 2 * lane + 1] = acc[h][1];
-      }
-    }
-    __syncthreads();
-    for (int e = tid; e < nc * (kD / 2); e += kThreads) {
-      const int col = e / (kD / 2);
-      const int dim = 2 * (e % (kD / 2));
-      float a0 = 0.f, a1 = 0.f;
-#pragma unroll
-      for (int w = 0; w < kNW; ++w) {
-        a0 += red[(w * 16 + col) * kD + dim];
-        a1 += red[(w * 16 + col) * kD + dim + 1];
-      }
-      write_out_pair(p, row_of(c0 + col), dim, a0, a1, s_L[col]);
+      write_out_pair(p, row, d, a0, a1, s_L[h]);
+      write_out_pair(p, row, d + 2, a2, a3, s_L[h]);
     }
   }
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
