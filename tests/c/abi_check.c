@@ -2,7 +2,9 @@
  * entry points behave as documented (no GPU is touched). Exit status 0 on
  * success; prints the first failed check otherwise. */
 #include <math.h>
+#include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "duo_attn.h"
@@ -56,6 +58,48 @@ int main(void) {
   CHECK(duo_attn_decode_block_workspace_bytes(&L, 4, 65, 1000) == 0); /* more than 64 tokens */
   r.theta = 1.f;
   CHECK(duo_rope_frequencies(&r, f) == DUO_ERR_INVALID_ARG);
+
+  /* work plans: count, then fill (4 int32 per item) */
+  {
+    int64_t n = 0;
+    CHECK(duo_prefill_plan(&L, 2, 300, 0, NULL, &n) == DUO_OK);
+    CHECK(n > 0 && n < 100000);
+    int32_t* items = (int32_t*)malloc((size_t)n * 4 * sizeof(int32_t));
+    CHECK(items != NULL);
+    CHECK(duo_prefill_plan(&L, 2, 300, 0, items, &n) == DUO_OK);
+    free(items);
+    int32_t split = 0;
+    CHECK(duo_decode_plan(&L, 3, 70000, &split, NULL, &n) == DUO_OK);
+    CHECK(split > 0 && n > 0);
+    items = (int32_t*)malloc((size_t)n * 4 * sizeof(int32_t));
+    CHECK(items != NULL);
+    CHECK(duo_decode_plan(&L, 3, 70000, &split, items, &n) == DUO_OK);
+    free(items);
+  }
+
+  /* launching calls refused on the host (bogus but aligned device addresses
+   * are never dereferenced on these paths) */
+  {
+    void* d = (void*)(uintptr_t)0x100000;
+    const int32_t* di = (const int32_t*)d;
+    duo_kv_cache c;
+    memset(&c, 0, sizeof c);
+    c.k_main = c.v_main = c.k_stream = c.v_stream = d;
+    c.main_capacity = 1000;
+    CHECK(duo_attn_prefill(&bad, NULL, 1, d, d, d, 16, 0, d, NULL, NULL, NULL, NULL) == DUO_ERR_UNSUPPORTED);
+    CHECK(duo_attn_prefill(&L, NULL, 1, d, d, d, 16, 5, d, NULL, NULL, NULL, NULL) == DUO_ERR_INVALID_ARG);
+    CHECK(duo_attn_prefill(&L, &c, 1, d, d, d, 16, 2000, d, NULL, NULL, NULL, NULL) == DUO_ERR_CAPACITY);
+    CHECK(duo_kv_append(&L, &c, 1, d, d, 16, di, 3, NULL, NULL) == DUO_ERR_INVALID_ARG);
+    CHECK(duo_kv_append(&L, &c, 1, d, d, 16, di, 5000, NULL, NULL) == DUO_ERR_CAPACITY);
+    CHECK(duo_attn_decode(&L, &c, 4, d, di, 1000, d, NULL, d, 16, NULL, NULL, NULL) == DUO_ERR_WORKSPACE);
+    CHECK(duo_attn_decode_block(&L, &c, 4, d, d, d, 65, di, 900, d, NULL, d, 1 << 20, NULL, NULL, NULL) == DUO_ERR_INVALID_ARG);
+    duo_epilogue e = {NULL, d, 7};
+    CHECK(duo_attn_prefill(&L, NULL, 1, d, d, d, 16, 0, d, NULL, NULL, &e, NULL) == DUO_ERR_INVALID_ARG);
+    duo_rope yr = {500000.f, 64.f, 4096, 64.f, 1.f, 1.f};
+    duo_prologue pro = {NULL, -1.f, &yr};
+    CHECK(duo_attn_prefill(&L, NULL, 1, d, d, d, 16, 0, d, NULL, &pro, NULL, NULL) == DUO_ERR_INVALID_ARG);
+    CHECK(strlen(duo_last_error()) > 0);
+  }
 
   /* empty calls are no-ops */
   CHECK(duo_attn_prefill(&L, NULL, 0, NULL, NULL, NULL, 0, 0, NULL, NULL, NULL, NULL, NULL) == DUO_OK);
