@@ -212,11 +212,12 @@ __device__ __forceinline__ f32x2 coherent_load2(const float* p) {
 
 // Output values (dim, dim + 1) of row bh: the unnormalised pair times the
 // row's normaliser and, if the call has one, the output gate.
+template <bool kFused>
 __device__ __forceinline__ void write_out_pair(const DecodeParams& p, int64_t bh, int dim, float a0, float a1,
                                                float inv) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   float f0 = inv, f1 = inv;
-  if (p.gate != nullptr) {
+  if (kFused && p.gate != nullptr) {
     if (p.gate_mode == 2) {
       const float gf = gate_factor(bf16_bits_to_f32(p.gate[bh]));
       f0 *= gf;
@@ -242,7 +243,7 @@ __device__ __forceinline__ void write_out_pair(const DecodeParams& p, int64_t bh
 // tiles in flight in registers: the same bytes in flight per CU as the
 // single-token kernel) into the slot's shared LDS tile, and each attends it
 // for its own 16 columns, so the cache is streamed once for 32 columns.
-template <bool kBlock, int kNH>
+template <bool kBlock, int kNH, bool kFused>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   static_assert(kNH == 1 || (kBlock && kNH == 2), "two halves only for the block decode");
   constexpr int kCols = 16 * kNH;
@@ -336,7 +337,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     }
     // RMSNorm + RoPE of q: the single-token query sits at len - 1, block
     // token t at past + t.
-    if (p.qpro_on) prologue_frag(qf, kBlock ? (int)len + (col0 + hc) / G : (int)len - 1, g, p.qpro);
+    if (kFused && p.qpro_on) prologue_frag(qf, kBlock ? (int)len + (col0 + hc) / G : (int)len - 1, g, p.qpro);
   }
 
   // Block decode: visibility of each key for this lane's query token.
@@ -498,8 +499,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     }
     const int64_t row = row_of(col);
     if (single) {
-      const RowNorm rn = row_norm(M, L, p.sink_logits, head_of(col));
-      write_out_pair(p, row, dim, a0, a1, rn.inv);
+      const RowNorm rn = row_norm(M, L, kFused ? p.sink_logits : nullptr, head_of(col));
+      write_out_pair<kFused>(p, row, dim, a0, a1, rn.inv);
       if (p.lse != nullptr && dim == 0) p.lse[row] = rn.lse;
     } else {
       const int64_t wslot = row * p.n_split_max + it.split;
@@ -560,7 +561,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 #pragma unroll
       for (int x = 32; x >= 1; x >>= 1) L += __shfl_xor(L, x);
       if (lane == 0) {
-        const RowNorm rn = row_norm(M, L, p.sink_logits, head_of(c0 + h));
+        const RowNorm rn = row_norm(M, L, kFused ? p.sink_logits : nullptr, head_of(c0 + h));
         s_L[h] = rn.inv;
         if (p.lse != nullptr) p.lse[row_of(c0 + h)] = rn.lse;
       }
@@ -595,16 +596,24 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
           a3 += w * hi[u].y;
         }
       }
-      write_out_pair(p, row, d, a0, a1, s_L[h]);
-      write_out_pair(p, row, d + 2, a2, a3, s_L[h]);
+      write_out_pair<kFused>(p, row, d, a0, a1, s_L[h]);
+      write_out_pair<kFused>(p, row, d + 2, a2, a3, s_L[h]);
     }
   }
   if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // next call
 }
 
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) { decode_body<false, 1>(p); }
-__global__ __launch_bounds__(256, 2) void decode_block16_kernel(DecodeParams p) { decode_body<true, 1>(p); }
-__global__ __launch_bounds__(512, 1) void decode_block_kernel(DecodeParams p) { decode_body<true, 2>(p); }
+// Plain kernels carry no prologue or epilogue code (it measurably slows the
+// plain path even when skipped); the fused ones are used when a call passes
+// a q prologue, sink logits or a gate.
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) { decode_body<false, 1, false>(p); }
+__global__ __launch_bounds__(256, 2) void decode_block16_kernel(DecodeParams p) { decode_body<true, 1, false>(p); }
+__global__ __launch_bounds__(512, 1) void decode_block_kernel(DecodeParams p) { decode_body<true, 2, false>(p); }
+__global__ __launch_bounds__(256, 2) void decode_fused_kernel(DecodeParams p) { decode_body<false, 1, true>(p); }
+__global__ __launch_bounds__(256, 2) void decode_block16_fused_kernel(DecodeParams p) { decode_body<true, 1, true>(p); }
+__global__ __launch_bounds__(512, 1) void decode_block_fused_kernel(DecodeParams p) { decode_body<true, 2, true>(p); }
+
+static bool fused(const DecodeParams& p) { return p.qpro_on || p.sink_logits != nullptr || p.gate != nullptr; }
 
 __global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -612,7 +621,8 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(int32_t* p, int64_t n) {
 }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
-  if (p.n_items > 0) hipLaunchKernelGGL(decode_kernel, dim3((unsigned)p.n_items), dim3(256), 0, s, p);
+  if (p.n_items > 0)
+    hipLaunchKernelGGL(fused(p) ? decode_fused_kernel : decode_kernel, dim3((unsigned)p.n_items), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -620,9 +630,11 @@ hipError_t launch_decode_block(const DecodeParams& p, hipStream_t s) {
   const int64_t items8 = ((int64_t)p.n_items + kXcds - 1) / kXcds * kXcds;
   if (p.n_items > 0) {
     if (p.T * p.group <= 16)  // one 16-column block: the 4-wave form
-      hipLaunchKernelGGL(decode_block16_kernel, dim3((unsigned)(items8 * p.n_cb)), dim3(256), 0, s, p);
+      hipLaunchKernelGGL(fused(p) ? decode_block16_fused_kernel : decode_block16_kernel,
+                         dim3((unsigned)(items8 * p.n_cb)), dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL(decode_block_kernel, dim3((unsigned)(items8 * p.n_cb)), dim3(512), 0, s, p);
+      hipLaunchKernelGGL(fused(p) ? decode_block_fused_kernel : decode_block_kernel,
+                         dim3((unsigned)(items8 * p.n_cb)), dim3(512), 0, s, p);
   }
   return hipGetLastError();
 }
