@@ -211,3 +211,51 @@ def test_block_decode_epilogue(lib, name):
     check_close(np.concatenate(got), o_ref, name)
     err = np.abs(np.concatenate(lgot) - l_ref).max()
     assert err < 1e-3, f"{name}: lse error {err}"
+
+
+def test_neutral_epilogue_matches_plain_kernels_bit_for_bit(lib):
+    """The fused kernels (taken whenever a call passes an epilogue) against the
+    plain ones: sink logits of -inf add nothing to the normaliser, and a
+    per-head gate of 100 has a sigmoid of exactly 1.0 in float32, so prefill,
+    multi-split decode and block decode must reproduce the plain outputs and
+    lse bit for bit."""
+    import torch
+    announce("neutral epilogue: fused kernels == plain kernels")
+    layer = lib.Layer(full_attention_heads=[1, 0, 0, 0, 1, 0, 0, 0])
+    hq, hkv = layer.num_q_heads, layer.num_kv_heads
+    B, P, T = 2, 9000, 200
+    N = P + T
+    q = wl.normal_tokens(91, wl.Q, B, 0, N, hq, 128)
+    k = wl.normal_tokens(91, wl.K, B, 0, N, hkv, 128)
+    v = wl.normal_tokens(91, wl.V, B, 0, N, hkv, 128)
+    sink = torch.full((hq,), float("-inf"), dtype=torch.float32, device="cuda")
+    cache = lib.KVCache(layer, B, N + 8)
+    sp0 = torch.zeros(B, dtype=torch.int32, device="cuda")
+    lib.kv_append(layer, cache, dev(k[:, :P]), dev(v[:, :P]), sp0, max_end_pos=P)
+
+    def both(run, out_shape, lse_shape):
+        res = []
+        for neutral in (False, True):
+            out = torch.empty(out_shape, dtype=torch.bfloat16, device="cuda")
+            lse = torch.empty(lse_shape, dtype=torch.float32, device="cuda")
+            gate = torch.full(out_shape[:-1], 100.0, dtype=torch.bfloat16, device="cuda") if neutral else None
+            run(out, lse, dict(sink_logits=sink, gate=gate) if neutral else {})
+            torch.cuda.synchronize()
+            res.append((host_bits(out), lse.cpu().numpy()))
+        (o0, l0), (o1, l1) = res
+        return np.array_equal(o0, o1) and np.array_equal(l0.view(np.uint32), l1.view(np.uint32))
+
+    qc, kc, vc = dev(q[:, P:]), dev(k[:, P:]), dev(v[:, P:])
+    assert both(lambda o, l, e: lib.attn_prefill(layer, qc, kc, vc, o, start_pos=P, past=cache, lse=l, **e),
+                (B, T, hq, 128), (B, hq, T)), "prefill"
+    seq = torch.tensor([P, 3000], dtype=torch.int32, device="cuda")
+    qd = dev(wl.decode_queries(92, B, hq, 128))
+    ws = lib.decode_workspace(layer, B, P)
+    assert lib.decode_plan(layer, B, P)[0] < P, "the decode should be multi-split"
+    assert both(lambda o, l, e: lib.attn_decode(layer, cache, qd, seq, P, o, ws, lse=l, **e),
+                (B, hq, 128), (B, hq)), "decode"
+    Tb = 4
+    qb, kb, vb = (dev(wl.normal_tokens(93, t, B, 0, Tb, h, 128)) for t, h in ((wl.Q, hq), (wl.K, hkv), (wl.V, hkv)))
+    wsb = lib.decode_block_workspace(layer, B, Tb, P)
+    assert both(lambda o, l, e: lib.attn_decode_block(layer, cache, qb, kb, vb, seq, P, o, wsb, lse=l, **e),
+                (B, Tb, hq, 128), (B, Tb, hq)), "block decode"
