@@ -311,9 +311,10 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
     const int hi = lo + kPrefillKeys - 1;
     const bool invisible = !wave_active || lo > qw1 || (r.span > 0 && hi < qw0 - r.span + 1);
 
-    // S^T = K Q^T for 64 keys x 16 kRT rows, at raised wave priority: the
-    // SIMD's other wave is then in its softmax or PV and yields issue slots
-    // to these MFMAs (2-3% faster on the 4 x 8192 prefill)
+    // S^T = K Q^T for 64 keys x 16 kRT rows, and the next tile's load issue,
+    // at raised wave priority: the SIMD's other wave is then in its softmax
+    // or PV and yields issue slots to these MFMAs (3-4% faster on the
+    // 4 x 8192 prefill)
     f32x4 s[kRT][4];
     if (!invisible) {
       __builtin_amdgcn_s_setprio(1);
@@ -332,8 +333,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
         }
       }
     }
-    __builtin_amdgcn_s_setprio(0);
     if (idx + 1 < ntiles) issue(idx + 1, nK, nV);
+    __builtin_amdgcn_s_setprio(0);
     if (!invisible) {
       const bool need_mask = !(lo >= r.lo && hi <= r.hi && hi <= qw0 && (r.span == 0 || lo >= qw1 - r.span + 1));
       if (need_mask) {
