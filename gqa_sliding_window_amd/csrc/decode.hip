@@ -131,6 +131,10 @@ template <bool kBlock>
 __device__ __forceinline__ void attend_tile(const uint16_t* sK, const uint16_t* sV, const bf16x8 (&qf)[4],
                                             int64_t k0, int64_t k_end, float c, int r16, int g, float& m,
                                             float& l, f32x4 (&o)[8], const BlockVis& bv, bool mask_all) {
+  // At raised wave priority, so that a wave with a tile to attend gets the
+  // issue slots before the SIMD's other wave, which is staging or waiting on
+  // loads (verify blocks of 36-48 columns 4% faster).
+  __builtin_amdgcn_s_setprio(1);
   f32x4 s[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
   for (int ds = 0; ds < 4; ++ds) {
@@ -192,6 +196,7 @@ __device__ __forceinline__ void attend_tile(const uint16_t* sK, const uint16_t* 
     const bf16x8 a = cat_bf16(lds_read_tr16(v0 + 16 * dt), lds_read_tr16(v1 + 16 * dt));
     o[dt] = mfma_16x16x32(a, pb, o[dt]);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Device-coherent (sc1) store / load: visible across XCDs without flushing
