@@ -89,6 +89,39 @@ class Timer:
         return mean
 
 
+def visible_pairs(layer, streaming: bool, start_pos: int, num_tokens: int) -> int:
+    """Sum over query positions i in [start_pos, start_pos + T) of |Vis(i)|,
+    from closed forms: i + 1 (causal), min(i + 1, W) (sliding window),
+    min(i + 1, S + R) (streaming head)."""
+    a, b = start_pos, start_pos + num_tokens - 1
+
+    def s_min(cap):  # sum over i in [a, b] of min(i + 1, cap)
+        tot = 0
+        hi_lin = min(b, cap - 1)
+        if hi_lin >= a:
+            tot += (a + 1 + hi_lin + 1) * (hi_lin - a + 1) // 2
+        flat_lo = max(a, cap)
+        if b >= flat_lo:
+            tot += cap * (b - flat_lo + 1)
+        return tot
+    if streaming:
+        return s_min(layer.sink + layer.recent)
+    if layer.main_ring:
+        return s_min(layer.window)
+    return (a + 1 + b + 1) * (b - a + 1) // 2
+
+
+def prefill_flops(G, layer, batch: int, num_tokens: int, start_pos: int = 0) -> int:
+    """Algorithmic FLOP of a prefill call: 4 * 128 per (query row, visible
+    key) pair over all batch x Hq rows; masked pairs are not counted. Head
+    classes come from the library's head-class plan."""
+    g = layer.num_q_heads // layer.num_kv_heads
+    classes = G.head_plan(layer)[0]
+    total = sum(g * visible_pairs(layer, classes[kvh] == 1, start_pos, num_tokens)
+                for kvh in range(layer.num_kv_heads))
+    return 4 * 128 * batch * total
+
+
 def dev_bits(torch, bits):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
 
@@ -102,10 +135,29 @@ def bench_prefill(torch, G, wl, timer, warmup, steps):
     qd, kd, vd = dev_bits(torch, q), dev_bits(torch, k), dev_bits(torch, v)
     out = torch.empty_like(qd)
     layer = G.Layer()
-    flops = G.prefill_flops(layer, w.batch, w.seq)
+    flops = prefill_flops(G, layer, w.batch, w.seq)
     log("prefill: timing")
     ms = timer.run(lambda i: G.attn_prefill(layer, qd, kd, vd, out), warmup, steps)
     return w, (q, k, v), flops, ms, (layer, qd, kd, vd, out)
+
+
+def bench_swa_prefill(torch, G, wl, timer, warmup, steps):
+    """The 1 x 1024 sliding-window prefill (12 query / 2 KV heads, window 512):
+    2.4 GFLOP in 96 workgroups, fewer than the 256 CUs, so its time is launch
+    and single-workgroup latency, not throughput."""
+    w = wl.WORKLOADS[1]
+    q = dev_bits(torch, wl.normal_tokens(w.seed, wl.Q, w.batch, 0, w.seq, w.hq, 128))
+    k = dev_bits(torch, wl.normal_tokens(w.seed, wl.K, w.batch, 0, w.seq, w.hkv, 128))
+    v = dev_bits(torch, wl.normal_tokens(w.seed, wl.V, w.batch, 0, w.seq, w.hkv, 128))
+    out = torch.empty_like(q)
+    layer = G.Layer(num_q_heads=w.hq, num_kv_heads=w.hkv, kind=G.SLIDING, window=w.window)
+    flops = prefill_flops(G, layer, w.batch, w.seq)
+    ms = timer.run(lambda i: G.attn_prefill(layer, q, k, v, out), warmup, steps)
+    wgs = len(G.prefill_plan(layer, w.batch, w.seq))
+    return {"workload": w.name, "algorithmic_flop": flops, "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "ms_median": timer.last["median_ms"], "ms_min": timer.last["min_ms"], "workgroups": wgs,
+            "bound": f"latency: {wgs} workgroups for 256 CUs, one short wave of work; "
+                     "no MFMA-peak target applies"}
 
 
 def bench_prologue_epilogue(torch, G, wl, timer, warmup, steps, w, flops, base_ms, devs):
@@ -243,30 +295,33 @@ def bench_chunked(torch, G, wl, timer, warmup, steps):
     out = torch.empty((n_chunks, 1, w.chunk, w.hq, 128), dtype=torch.bfloat16, device="cuda")
     cache = G.KVCache(layer, 1, w.seq, zero=False)
     starts = [torch.tensor([c * w.chunk], dtype=torch.int32, device="cuda") for c in range(n_chunks)]
-    flops = sum(G.prefill_flops(layer, 1, w.chunk, c * w.chunk) for c in range(n_chunks))
+    flops = sum(prefill_flops(G, layer, 1, w.chunk, c * w.chunk) for c in range(n_chunks))
+    # one prefill workspace for every chunk: the library cuts the full-context
+    # query tiles of a chunk over a long past into key-range pieces
+    ws = G.prefill_workspace(layer, 1, w.chunk, [c * w.chunk for c in range(n_chunks)])
+    pieces = [int(G.prefill_plan(layer, 1, w.chunk, c * w.chunk, True)[:, 5].max()) for c in range(n_chunks)]
 
     def one_pass(_):
         for c in range(n_chunks):
-            G.attn_prefill(layer, q[c], k[c], v[c], out[c], start_pos=c * w.chunk, past=cache)
+            G.attn_prefill(layer, q[c], k[c], v[c], out[c], start_pos=c * w.chunk, past=cache, workspace=ws)
             G.kv_append(layer, cache, k[c], v[c], starts[c], max_end_pos=(c + 1) * w.chunk)
 
     log("chunked prefill: timing passes")
     ms = timer.run(one_pass, warmup, steps)
     pass_stats = dict(timer.last)
-    # attention-only: per-chunk prefill calls alone, cache already filled
-    s = torch.cuda.current_stream()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n_chunks)]
-    torch.cuda.synchronize()
-    for c in range(n_chunks):
-        ev[2 * c].record(s)
-        G.attn_prefill(layer, q[c], k[c], v[c], out[c], start_pos=c * w.chunk, past=cache)
-        ev[2 * c + 1].record(s)
-    torch.cuda.synchronize()
-    attn_ms = sum(ev[2 * c].elapsed_time(ev[2 * c + 1]) for c in range(n_chunks))
+    # attention alone: the 16 prefill calls of a pass without their appends
+    # (the cache already holds every position), timed like the passes
+    def attend_only(_):
+        for c in range(n_chunks):
+            G.attn_prefill(layer, q[c], k[c], v[c], out[c], start_pos=c * w.chunk, past=cache, workspace=ws)
+
+    log("chunked prefill: timing the attention calls alone")
+    attn_ms = timer.run(attend_only, warmup, steps)
     # cache manager on one chunk: read 2 x chunk rows, write 2 x chunk rows
     app_ms = timer.run(lambda i: G.kv_append(layer, cache, k[0], v[0], starts[0], max_end_pos=w.chunk), 2, 20)
     app_bytes = 2 * 2 * w.chunk * w.hkv * 128 * 2
-    return w, mask, flops, ms, attn_ms, app_ms, app_bytes, pass_stats
+    ws_bytes = 0 if ws is None else ws.numel() * 4
+    return w, mask, flops, ms, attn_ms, app_ms, app_bytes, pass_stats, pieces, ws_bytes
 
 
 def bench_copy(torch, timer, warmup, steps, nbytes=1 << 30):
@@ -313,34 +368,80 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(w, qkv, target_s, total_flop):
-    """Time the float64 oracle on a bounded sample of the headline workload
-    on one host thread (its per-row products are too small to gain from BLAS
-    threads: 16 threads measured slower than one)."""
+ORACLE_ROWS = 1 << 18  # sample of the headline workload drawn for the oracle baseline
+
+
+def oracle_worker(idx: int, nproc: int, target_s: float):
+    """One process of the oracle baseline: the sampled rows of the (batch,
+    KV head) groups g with g % nproc == idx, in random order within each
+    group, until target_s seconds of oracle time have passed. Prints one JSON
+    line (rows, FLOP, seconds). Inputs are regenerated from the workload's
+    seeds for the batch rows this process needs."""
     import threadpoolctl
     import oracle
     import workloads as wl
-    q, k, v = qkv
-    threads = 1
-    rows = wl.sample_query_rows(w, w.seq, 32768)
-    rng = np.random.default_rng(0)
-    rows = rows[rng.permutation(len(rows))]
-    done = 0
-    flops = 0
-    t0 = time.perf_counter()
-    with threadpoolctl.threadpool_limits(threads):
-        while done < len(rows) and time.perf_counter() - t0 < target_s:
-            batch = rows[done:done + 64]
-            batch = batch[np.lexsort((batch[:, 2], batch[:, 1], batch[:, 0]))]
-            oracle.prefill_rows(q, k, v, 0, batch, hkv=w.hkv, layer="full")
-            flops += int(4 * 128 * (batch[:, 2] + 1).sum())
-            done += len(batch)
-    dt = time.perf_counter() - t0
-    rate = flops / dt
-    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} seeded query rows of the headline workload (float64, {threads} "
-                      f"thread), {dt:.1f} s", "rows_per_s": done / dt,
-            "extrapolated_full_workload_s": total_flop / rate}
+    w = wl.WORKLOADS[2]
+    G = w.hq // w.hkv
+    rows = wl.sample_query_rows(w, w.seq, ORACLE_ROWS)
+    grp = rows[:, 0] * w.hkv + rows[:, 1] // G
+    mine = [g for g in range(w.batch * w.hkv) if g % nproc == idx]
+    rng = np.random.default_rng(idx)
+    done = flops = 0
+    spent = 0.0
+    with threadpoolctl.threadpool_limits(1):
+        for g in mine:
+            b = g // w.hkv
+            counts = [w.seq if i == b else 0 for i in range(w.batch)]
+            qb = np.stack([x if len(x) else np.zeros((w.seq, w.hq, 128), np.uint16) for x in
+                           wl.normal_tokens_ragged(w.seed, wl.Q, [0] * w.batch, counts, w.hq, 128, threads=1)])
+            kb = np.stack([x if len(x) else np.zeros((w.seq, w.hkv, 128), np.uint16) for x in
+                           wl.normal_tokens_ragged(w.seed, wl.K, [0] * w.batch, counts, w.hkv, 128, threads=1)])
+            vb = np.stack([x if len(x) else np.zeros((w.seq, w.hkv, 128), np.uint16) for x in
+                           wl.normal_tokens_ragged(w.seed, wl.V, [0] * w.batch, counts, w.hkv, 128, threads=1)])
+            sel = rows[grp == g]
+            sel = sel[rng.permutation(len(sel))]
+            t0 = time.perf_counter()
+            for s0 in range(0, len(sel), 16):
+                part = sel[s0:s0 + 16]
+                oracle.prefill_rows(qb, kb, vb, 0, part, hkv=w.hkv, layer="full")
+                flops += int(4 * 128 * (part[:, 2] + 1).sum())
+                done += len(part)
+                if spent + time.perf_counter() - t0 >= target_s:
+                    break
+            spent += time.perf_counter() - t0
+            if spent >= target_s:
+                break
+    print(json.dumps({"rows": done, "flop": flops, "seconds": spent}), flush=True)
+
+
+def cpu_baseline(target_s, total_flop):
+    """Time the float64 oracle on the host cores: one single-threaded process
+    per core of this process's CPU set (at most 16, the host share of one
+    GPU), each taking the sampled rows of its own (batch, KV head) groups.
+    Reports the aggregate rate and, labelled as such, its extrapolation to
+    the whole headline workload."""
+    import subprocess
+    affinity = len(os.sched_getaffinity(0))
+    nproc = max(1, min(16, affinity))
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    procs = [subprocess.Popen([sys.executable, os.path.abspath(__file__), "--oracle-worker", str(i), str(nproc),
+                               str(target_s)], stdout=subprocess.PIPE, env=env, cwd=HERE) for i in range(nproc)]
+    res = []
+    for p in procs:
+        out, _ = p.communicate()
+        if p.returncode != 0:
+            raise RuntimeError(f"oracle worker failed with status {p.returncode}")
+        res.append(json.loads(out.decode().strip().splitlines()[-1]))
+    rows = sum(r["rows"] for r in res)
+    flops = sum(r["flop"] for r in res)
+    rate = sum(r["flop"] / r["seconds"] for r in res if r["seconds"] > 0)
+    secs = max(r["seconds"] for r in res)
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": nproc, "kind": "oracle",
+            "sample": f"{rows} seeded query rows of the headline workload, float64, {nproc} single-threaded "
+                      f"processes split by (batch, KV head), {secs:.1f} s each",
+            "host_cpus_in_affinity": affinity, "rows_per_s": rows / secs, "flop": flops,
+            "extrapolated_full_workload_s": total_flop / rate,
+            "extrapolation": "the headline workload's algorithmic FLOP divided by the sampled rate"}
 
 
 def main():
@@ -348,11 +449,17 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sections", default="prefill,sliding,prologue,decode,chunked",
-                    help="comma list of prefill, sliding and prologue (both need prefill), decode, chunked, "
+    ap.add_argument("--sections", default="prefill,sliding,swa,prologue,decode,chunked",
+                    help="comma list of prefill, sliding and prologue (both need prefill), swa (the 1 x 1024 "
+                         "sliding prefill), decode, chunked, "
                          "copy (copy = counter calibration: a plain 1 GiB device copy)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget (0 = skip)")
+    ap.add_argument("--oracle-worker", nargs=3, metavar=("IDX", "NPROC", "SECONDS"), help=argparse.SUPPRESS)
     args = ap.parse_args()
+    if args.oracle_worker:
+        i, n, t = args.oracle_worker
+        oracle_worker(int(i), int(n), float(t))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this path runs without sharding or collectives; "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)
@@ -397,7 +504,7 @@ def main():
         # the same shape on a 512-token sliding-window layer (30 of the model's
         # 40 layers are of this kind)
         layer_s = G.Layer(kind=G.SLIDING, window=512)
-        fl_s = G.prefill_flops(layer_s, w2.batch, w2.seq)
+        fl_s = prefill_flops(G, layer_s, w2.batch, w2.seq)
         lq, qd_, kd_, vd_, od_ = devs
         ms_s = timer.run(lambda i: G.attn_prefill(layer_s, qd_, kd_, vd_, od_), args.warmup, args.steps)
         res["sliding_prefill"] = {"workload": w2.name + " on a sliding-window layer (w 512)",
@@ -405,6 +512,9 @@ def main():
                                   "TFLOP/s": fl_s / (ms_s * 1e-3) / 1e12,
                                   "ms_median": timer.last["median_ms"], "ms_min": timer.last["min_ms"]}
         log(f"sliding prefill: {ms_s:.3f} ms, {res['sliding_prefill']['TFLOP/s']:.1f} TFLOP/s")
+    if "swa" in sections:
+        res["swa_prefill"] = bench_swa_prefill(torch, G, wl, timer, args.warmup, args.steps)
+        log(f"swa prefill (1x1024, 12/2 heads, w 512): {res['swa_prefill']['ms'] * 1e3:.1f} us")
     if "prologue" in sections and devs is not None:
         res["prologue_epilogue"] = bench_prologue_epilogue(torch, G, wl, timer, args.warmup, args.steps, w2,
                                                            flops, ms, devs)
@@ -431,11 +541,12 @@ def main():
         res["decode"] = d
 
     if "chunked" in sections:
-        w5, mask5, fl5, ms5, attn5, app_ms, app_bytes, st5 = bench_chunked(torch, G, wl, timer, 1,
-                                                                          max(1, args.steps // 10))
+        w5, mask5, fl5, ms5, attn5, app_ms, app_bytes, st5, pieces5, ws5 = bench_chunked(
+            torch, G, wl, timer, 1, max(1, args.steps // 10))
         res["chunked_prefill"] = {"workload": w5.name, "mask": mask5, "algorithmic_flop": fl5,
                                   "ms_total": ms5, "TFLOP/s": fl5 / (ms5 * 1e-3) / 1e12,
                                   "ms_total_median": st5["median_ms"], "ms_total_min": st5["min_ms"],
+                                  "pieces_per_chunk": pieces5, "prefill_workspace_bytes": ws5,
                                   "attention_only_ms": attn5,
                                   "attention_only_TFLOP/s": fl5 / (attn5 * 1e-3) / 1e12}
         res["kv_append"] = {"workload": "one 8192-token chunk, 8 KV heads", "ms": app_ms,
@@ -451,7 +562,7 @@ def main():
 
     if w2 is not None and args.cpu_seconds > 0:
         log("cpu baseline: timing the oracle")
-        res["cpu_baseline"] = cpu_baseline(w2, qkv, args.cpu_seconds, res["config"]["algorithmic_flop_per_step"])
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds, res["config"]["algorithmic_flop_per_step"])
     print(json.dumps(res), flush=True)
 
 

@@ -111,7 +111,8 @@ def load(path: str = LIB_PATH):
     I32P, I64P = ctypes.POINTER(i32), ctypes.POINTER(i64)
     sigs = {
         "duo_kv_append": (ctypes.c_int, [LP, CP, i32, P, P, i32, P, i64, PP, P]),
-        "duo_attn_prefill": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, i64, P, P, PP, EP, P]),
+        "duo_attn_prefill": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, i64, P, P, P, sz, PP, EP, P]),
+        "duo_attn_prefill_workspace_bytes": (sz, [LP, i32, i32, i64]),
         "duo_attn_decode": (ctypes.c_int, [LP, CP, i32, P, P, i64, P, P, P, sz, PP, EP, P]),
         "duo_qk_prologue": (ctypes.c_int, [PP, i32, i32, i32, P, P, P, P]),
         "duo_rope_frequencies": (ctypes.c_int, [ctypes.POINTER(_Rope), ctypes.POINTER(ctypes.c_double)]),
@@ -122,7 +123,7 @@ def load(path: str = LIB_PATH):
         "duo_kv_cache_bytes": (ctypes.c_int, [LP, i32, i64, I64P, I64P]),
         "duo_kv_cache_report": (ctypes.c_int, [LP, i32, i64, I32P, ctypes.POINTER(_CacheReport)]),
         "duo_head_plan": (ctypes.c_int, [LP, I32P, I32P, I32P, I32P]),
-        "duo_prefill_plan": (ctypes.c_int, [LP, i32, i32, i64, I32P, I64P]),
+        "duo_prefill_plan": (ctypes.c_int, [LP, i32, i32, i64, i32, I32P, I64P]),
         "duo_decode_plan": (ctypes.c_int, [LP, i32, i64, I32P, I32P, I64P]),
         "duo_last_error": (ctypes.c_char_p, []),
         "duo_attn_version": (ctypes.c_int, []),
@@ -164,13 +165,13 @@ class Layer:
 
     @property
     def n_main(self) -> int:
-        if self.full_attention_heads is None:
-            return self.num_kv_heads
-        return sum(1 for x in self.full_attention_heads if int(x) != 0)
+        """Full-context KV heads, from the library's head-class plan."""
+        return head_plan(self)[2]
 
     @property
     def n_stream(self) -> int:
-        return self.num_kv_heads - self.n_main
+        """Streaming KV heads, from the library's head-class plan."""
+        return head_plan(self)[3]
 
     @property
     def main_ring(self) -> bool:
@@ -222,9 +223,37 @@ def _need_batch(t, name: str, batch: int):
         raise ValueError(f"{name}: leading extent {t.shape[0]} < batch {batch}")
 
 
-def _need_cache(cache, batch: int, batch_offset: int = 0):
-    if isinstance(cache, KVCache) and (batch_offset < 0 or batch_offset + batch > cache.batch):
+def _cache_geometry(layer: "Layer"):
+    """What fixes a cache's extents and slot contract for a layer: KV heads,
+    which of them stream, the ring of a sliding layer, sink and recent."""
+    streaming = tuple(c == 1 for c in head_plan(layer)[0])
+    return {"num_kv_heads": layer.num_kv_heads, "streaming_heads": streaming, "main_ring": layer.main_ring,
+            "window": layer.window if layer.main_ring else 0, "sink": layer.sink, "recent": layer.recent}
+
+
+def _need_cache(cache, layer: "Layer", batch: int, batch_offset: int = 0):
+    """A KVCache used by a call must cover its batch rows and have been built
+    for a layer with the same head classes and sizes: the C ABI receives bare
+    pointers, and a cache with fewer heads of a class, a shorter sink + recent
+    ring or another window would be read and written past its tensors."""
+    if not isinstance(cache, KVCache):
+        return
+    if batch_offset < 0 or batch_offset + batch > cache.batch:
         raise ValueError(f"cache holds {cache.batch} sequences; the call uses [{batch_offset}, {batch_offset + batch})")
+    want, have = _cache_geometry(layer), _cache_geometry(cache.layer)
+    diff = [k for k in want if want[k] != have[k]]
+    if diff:
+        raise ValueError("cache was built for another layer geometry: "
+                         + ", ".join(f"{k} {have[k]} (call: {want[k]})" for k in diff))
+    nm, ns, sr = layer.n_main, layer.n_stream, layer.sink + layer.recent
+    for t, name, shape in ((cache.k_main, "k_main", (cache.batch, nm, cache.capacity, HEAD_DIM)),
+                           (cache.v_main, "v_main", (cache.batch, nm, cache.capacity, HEAD_DIM)),
+                           (cache.k_stream, "k_stream", (cache.batch, ns, sr, HEAD_DIM)),
+                           (cache.v_stream, "v_stream", (cache.batch, ns, sr, HEAD_DIM))):
+        if shape[1] == 0:
+            continue
+        if t is None or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"cache.{name}: {None if t is None else tuple(t.shape)}, expected {shape} contiguous")
 
 
 def _need_prologue(pro, name: str):
@@ -278,7 +307,7 @@ def kv_append(layer: Layer, cache: KVCache, k_new, v_new, start_pos, max_end_pos
     _need(start_pos, "start_pos", (None,), "int32")
     for t, n in ((k_new, "k_new"), (v_new, "v_new"), (start_pos, "start_pos")):
         _need_batch(t, n, B)
-    _need_cache(cache, B, batch_offset)
+    _need_cache(cache, layer, B, batch_offset)
     _need_prologue(k_prologue, "k_prologue")
     _need_device(k_new=k_new, v_new=v_new, start_pos=start_pos)
     lib = load()
@@ -335,9 +364,12 @@ def _epilogue(out, sink_logits, gate):
 
 
 def attn_prefill(layer: Layer, q, k, v, out, start_pos: int = 0, past: Optional[KVCache] = None,
-                 lse=None, stream=None, sink_logits=None, gate=None, q_prologue: Optional[Prologue] = None):
+                 lse=None, stream=None, sink_logits=None, gate=None, q_prologue: Optional[Prologue] = None,
+                 workspace=None):
     """duo_attn_prefill: q [B, T, Hq, 128], k/v [B, T, Hkv, 128], out like q;
-    optional attention-sink logits and output gate (see _epilogue)."""
+    optional attention-sink logits and output gate (see _epilogue); an
+    optional zero-initialised workspace (prefill_workspace) lets the library
+    cut long query tiles into key-range pieces."""
     B, T = q.shape[0], q.shape[1]
     hq, hkv = layer.num_q_heads, layer.num_kv_heads
     _need(q, "q", (B, T, hq, HEAD_DIM), "bfloat16")
@@ -347,15 +379,35 @@ def attn_prefill(layer: Layer, q, k, v, out, start_pos: int = 0, past: Optional[
     _need(lse, "lse", (B, hq, T), "float32")
     _need_prologue(q_prologue, "q_prologue")
     if past is not None:
-        _need_cache(past, B)
+        _need_cache(past, layer, B)
     epi = _epilogue(out, sink_logits, gate)
-    _need_device(q=q, k=k, v=v, out=out, lse=lse)
+    _need(workspace, "workspace", None, "float32")
+    _need_device(q=q, k=k, v=v, out=out, lse=lse, workspace=workspace)
     lib = load()
     cl = layer._c()
     cc = past._c() if past is not None else None
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.duo_attn_prefill(ctypes.byref(cl), ctypes.byref(cc) if cc is not None else None, B,
                                 _ptr(q), _ptr(k), _ptr(v), T, int(start_pos), _ptr(out), _ptr(lse),
-                                _prologue(q_prologue), epi, _stream(stream)))
+                                _ptr(workspace), nbytes, _prologue(q_prologue), epi, _stream(stream)))
+
+
+def prefill_workspace_bytes(layer: Layer, batch: int, num_tokens: int, start_pos: int = 0) -> int:
+    """duo_attn_prefill_workspace_bytes (0: no query tile would be cut)."""
+    cl = layer._c()
+    return int(load().duo_attn_prefill_workspace_bytes(ctypes.byref(cl), batch, int(num_tokens), int(start_pos)))
+
+
+def prefill_workspace(layer: Layer, batch: int, num_tokens: int, start_positions, device="cuda"):
+    """A zero-filled prefill workspace large enough for chunks of num_tokens
+    tokens at each of the given start positions (None if none needs one)."""
+    import torch
+    need = max(prefill_workspace_bytes(layer, batch, num_tokens, int(p)) for p in start_positions)
+    if need == 0:
+        return None
+    ws = torch.empty((need + 3) // 4, dtype=torch.float32, device=device)
+    init_decode_workspace(ws)
+    return ws
 
 
 def decode_workspace_bytes(layer: Layer, batch: int, max_seq_len: int) -> int:
@@ -389,7 +441,7 @@ def attn_decode(layer: Layer, cache: KVCache, q, seq_lens, max_seq_len: int, out
     _need(lse, "lse", (B, hq), "float32")
     _need(workspace, "workspace", None, "float32")
     _need_prologue(q_prologue, "q_prologue")
-    _need_cache(cache, B)
+    _need_cache(cache, layer, B)
     epi = _epilogue(out, sink_logits, gate)
     _need_device(q=q, seq_lens=seq_lens, out=out, lse=lse, workspace=workspace)
     lib = load()
@@ -430,7 +482,7 @@ def attn_decode_block(layer: Layer, cache: KVCache, q, k_new, v_new, past_lens, 
     _need(lse, "lse", (B, T, hq), "float32")
     _need(workspace, "workspace", None, "float32")
     _need_prologue(q_prologue, "q_prologue")
-    _need_cache(cache, B)
+    _need_cache(cache, layer, B)
     epi = _epilogue(out, sink_logits, gate)
     _need_device(q=q, k_new=k_new, v_new=v_new, past_lens=past_lens, out=out, lse=lse, workspace=workspace)
     lib = load()
@@ -456,15 +508,17 @@ def prefill_tile_rows() -> int:
     return int(load().duo_prefill_tile_rows())
 
 
-def prefill_plan(layer: Layer, batch: int, num_tokens: int, start_pos: int = 0):
-    """Per workgroup (batch, q_head, q_tile, key_tiles); padding rows are -1."""
+def prefill_plan(layer: Layer, batch: int, num_tokens: int, start_pos: int = 0, with_workspace: bool = False):
+    """Per workgroup (batch, q_head, q_tile, key_tiles, piece, pieces);
+    padding rows are (-1, -1, -1, 0, 0, 0)."""
     import numpy as np
     lib = load()
     cl = layer._c()
     n = ctypes.c_int64()
-    _check(lib.duo_prefill_plan(ctypes.byref(cl), batch, num_tokens, start_pos, None, ctypes.byref(n)))
-    items = np.zeros((n.value, 4), dtype=np.int32)
-    _check(lib.duo_prefill_plan(ctypes.byref(cl), batch, num_tokens, start_pos,
+    ws = 1 if with_workspace else 0
+    _check(lib.duo_prefill_plan(ctypes.byref(cl), batch, num_tokens, start_pos, ws, None, ctypes.byref(n)))
+    items = np.zeros((n.value, 6), dtype=np.int32)
+    _check(lib.duo_prefill_plan(ctypes.byref(cl), batch, num_tokens, start_pos, ws,
                                 items.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(n)))
     return items
 
@@ -509,36 +563,3 @@ def kv_cache_report(layer: Layer, batch: int, capacity: int, seq_lens) -> dict:
     _check(lib.duo_kv_cache_report(ctypes.byref(cl), batch, capacity,
                                    lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(rep)))
     return {n: getattr(rep, n) for n, _ in _CacheReport._fields_}
-
-
-def prefill_flops(layer: Layer, batch: int, num_tokens: int, start_pos: int = 0) -> int:
-    """Algorithmic FLOP: 4 * D per (query row, visible key) pair, over all
-    batch x Hq rows (masked pairs are not counted)."""
-    g = layer.num_q_heads // layer.num_kv_heads
-    total = 0
-    for kvh in range(layer.num_kv_heads):
-        streaming = layer.full_attention_heads is not None and int(layer.full_attention_heads[kvh]) == 0
-        total += g * visible_pairs(layer, streaming, start_pos, num_tokens)
-    return 4 * HEAD_DIM * batch * total
-
-
-def visible_pairs(layer: Layer, streaming: bool, start_pos: int, num_tokens: int) -> int:
-    """Sum over query positions i in [start_pos, start_pos+T) of |Vis(i)|
-    (closed forms: min(i+1, W), min(i+1, S+R) or i+1)."""
-    def s_min(cap):  # sum_{i=a}^{b} min(i+1, cap)
-        a, b = start_pos, start_pos + num_tokens - 1
-        tot = 0
-        lo_lin = a
-        hi_lin = min(b, cap - 1)
-        if hi_lin >= lo_lin:
-            tot += (lo_lin + 1 + hi_lin + 1) * (hi_lin - lo_lin + 1) // 2
-        flat_lo = max(a, cap)
-        if b >= flat_lo:
-            tot += cap * (b - flat_lo + 1)
-        return tot
-    if streaming:
-        return s_min(layer.sink + layer.recent)
-    if layer.main_ring:
-        return s_min(layer.window)
-    a, b = start_pos, start_pos + num_tokens - 1
-    return (a + 1 + b + 1) * (b - a + 1) // 2

@@ -191,7 +191,56 @@ int read_epilogue(const duo_epilogue* e, const float** sink, const uint16_t** ga
 }
 
 // ---- prefill plan
-int build_prefill(const Layer& L, int32_t batch, int32_t T, int64_t start_pos, PrefillParams* p,
+// Key-range pieces per main unit. A long main unit (a chunk's full-context
+// query tile over a long past) can outlast the rest of the launch: with few
+// such units per resident workgroup slot, the last round of them runs on a
+// part of the GPU. When the longest main unit holds more than half the work
+// per slot, the plan cuts every main unit into n pieces, n chosen to minimise
+// the estimated makespan max(rounds of pieces x piece length, total work /
+// slots), each piece costing kPieceCost more tile-steps and holding at least
+// kMinPieceTiles key tiles; otherwise n = 1.
+int choose_pieces(const PrefillParams& p) {
+  if (p.n_main == 0 || p.n_qtiles > 65536) return 1;
+  int64_t wm = 0, ws = 0, lmax = 0;
+  const int64_t last = p.start_pos + p.T - 1;
+  for (int qt = 0; qt < p.n_qtiles; ++qt) {
+    const int64_t qa = p.start_pos + (int64_t)qt * kPrefillRows;
+    const int64_t qb = qa + kPrefillRows - 1 < last ? qa + kPrefillRows - 1 : last;
+    KeyRange r0, r1;
+    prefill_key_ranges(p, kMain, qa, qb, r0, r1);
+    const int64_t nm = tiles_of(r0);
+    wm += nm;
+    lmax = nm > lmax ? nm : lmax;
+    if (p.n_stream > 0) {
+      const int nr = prefill_key_ranges(p, kStream, qa, qb, r0, r1);
+      ws += (nr > 0 ? tiles_of(r0) : 0) + (nr > 1 ? tiles_of(r1) : 0);
+    }
+  }
+  const int64_t per_qt_main = (int64_t)p.batch * p.n_main * p.group;  // workgroups per query tile
+  const int64_t total = (wm * p.n_main + ws * p.n_stream) * p.batch * p.group;
+  const int64_t nm_wg = per_qt_main * p.n_qtiles;
+  if (lmax * 2 * kPrefillSlots <= total) return 1;
+  auto est = [&](int n) {
+    const int64_t rounds = (nm_wg * n + kPrefillSlots - 1) / kPrefillSlots;
+    const int64_t piece = (lmax + n - 1) / n + (n > 1 ? kPieceCost : 0);
+    const int64_t spread = (total + (n > 1 ? nm_wg * n * kPieceCost : 0)) / kPrefillSlots;
+    return rounds * piece > spread ? rounds * piece : spread;
+  };
+  int best = 1;
+  int64_t best_est = est(1);
+  for (int n = 2; n <= kMaxPieces && lmax >= (int64_t)n * kMinPieceTiles; ++n) {
+    const int64_t e = est(n);
+    if (e * 50 < best_est * 49) {  // at least 2% better
+      best = n;
+      best_est = e;
+    }
+  }
+  return best;
+}
+
+// split = false: every unit in one workgroup (no workspace); true: the
+// key-range pieces of choose_pieces.
+int build_prefill(const Layer& L, int32_t batch, int32_t T, int64_t start_pos, bool split, PrefillParams* p,
                   int64_t* n_blocks) {
   std::memset(p, 0, sizeof(*p));
   p->start_pos = start_pos;
@@ -210,14 +259,31 @@ int build_prefill(const Layer& L, int32_t batch, int32_t T, int64_t start_pos, P
   p->n_qtiles = (T + kPrefillRows - 1) / kPrefillRows;
   const int64_t um = (int64_t)p->n_qtiles * batch * L.plan.n_main;
   const int64_t us = (int64_t)p->n_qtiles * batch * L.plan.n_stream;
-  if (um + us > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "prefill work too large for one launch");
+  if (um + us + kXcds > kMaxGrid / kMaxPieces) return fail(DUO_ERR_INVALID_ARG, "prefill work too large for one launch");
   p->n_units_main = (int32_t)um;
   p->n_units = (int32_t)(um + us);
+  p->n_units_main8 = (int32_t)((um + kXcds - 1) / kXcds * kXcds);
+  p->n_pieces = split ? choose_pieces(*p) : 1;
   p->scale_log2 = L.scale * 1.4426950408889634f;
-  const int64_t units8 = (p->n_units + kXcds - 1) / kXcds * kXcds;
+  const int64_t virt = (int64_t)p->n_units_main8 * p->n_pieces + us;
+  const int64_t units8 = (virt + kXcds - 1) / kXcds * kXcds;
   *n_blocks = units8 * L.group;
   if (*n_blocks > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "prefill grid too large");
   return DUO_OK;
+}
+
+// Prefill workspace: [n_units_main * group] int32 arrival counters |
+// [n_units_main * group * n_pieces] partial results of kPartFloats floats;
+// both parts 256-byte aligned. Empty without pieces.
+struct PrefillWs { size_t part, total; };
+
+PrefillWs prefill_ws_layout(const PrefillParams& p) {
+  PrefillWs w{0, 0};
+  if (p.n_pieces <= 1) return w;
+  const size_t slots = (size_t)p.n_units_main * p.group;
+  w.part = (slots * sizeof(int32_t) + 255) / 256 * 256;
+  w.total = w.part + slots * p.n_pieces * (size_t)kPartFloats * sizeof(float);
+  return w;
 }
 
 // ---- decode plan: keys per workgroup split chosen so the launch has about
@@ -400,7 +466,7 @@ int duo_kv_append(const duo_layer* layer, const duo_kv_cache* cache, int32_t bat
 }
 
 int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens, int64_t start_pos,
-                     int32_t* items, int64_t* n_items) {
+                     int32_t with_workspace, int32_t* items, int64_t* n_items) {
   Layer L;
   int rc = check_layer(layer, &L);
   if (rc) return rc;
@@ -408,29 +474,47 @@ int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens, 
   if (start_pos + num_tokens > kMaxPos) return fail(DUO_ERR_INVALID_ARG, "positions exceed %lld", (long long)kMaxPos);
   PrefillParams p;
   int64_t nb = 0;
-  if (batch > 0 && num_tokens > 0 && (rc = build_prefill(L, batch, num_tokens, start_pos, &p, &nb))) return rc;
+  if (batch > 0 && num_tokens > 0 &&
+      (rc = build_prefill(L, batch, num_tokens, start_pos, with_workspace != 0, &p, &nb)))
+    return rc;
   if (n_items) *n_items = nb;
   if (items) {
     for (int64_t i = 0; i < nb; ++i) {
       const PrefillItem it = prefill_item(p, (int)i);
-      int32_t* o = items + 4 * i;
-      if (!it.valid) { o[0] = o[1] = o[2] = -1; o[3] = 0; continue; }
+      int32_t* o = items + 6 * i;
+      o[0] = o[1] = o[2] = -1;
+      o[3] = o[4] = 0;
+      o[5] = 0;
+      if (!it.valid) continue;
       const int64_t qa = start_pos + (int64_t)it.qtile * kPrefillRows;
       const int64_t last = start_pos + num_tokens - 1;
       const int64_t qb = qa + kPrefillRows - 1 < last ? qa + kPrefillRows - 1 : last;
       KeyRange r0, r1;
       const int nr = prefill_key_ranges(p, it.cls, qa, qb, r0, r1);
       const int64_t tiles = tiles_of(r0) + (nr > 1 ? tiles_of(r1) : 0);
-      o[0] = it.b; o[1] = it.qhead; o[2] = it.qtile; o[3] = (int32_t)tiles;
+      const PieceRange pr = piece_range((int)tiles, it.cls == kMain ? p.n_pieces : 1, it.piece);
+      o[0] = it.b; o[1] = it.qhead; o[2] = it.qtile; o[3] = pr.t1 - pr.t0; o[4] = it.piece; o[5] = pr.used;
     }
   }
   return ok();
 }
 
+size_t duo_attn_prefill_workspace_bytes(const duo_layer* layer, int32_t batch, int32_t num_tokens,
+                                        int64_t start_pos) {
+  Layer L;
+  if (check_layer(layer, &L)) return 0;
+  if (batch <= 0 || num_tokens <= 0 || start_pos < 0 || start_pos + num_tokens > kMaxPos) return 0;
+  PrefillParams p;
+  int64_t nb = 0;
+  if (build_prefill(L, batch, num_tokens, start_pos, true, &p, &nb)) return 0;
+  ok();
+  return prefill_ws_layout(p).total;
+}
+
 int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t batch, const void* q,
                      const void* k, const void* v, int32_t num_tokens, int64_t start_pos, void* out,
-                     float* lse, const duo_prologue* q_prologue, const duo_epilogue* epilogue,
-                     void* stream) {
+                     float* lse, void* workspace, size_t workspace_bytes, const duo_prologue* q_prologue,
+                     const duo_epilogue* epilogue, void* stream) {
   Layer L;
   int rc = check_layer(layer, &L);
   if (rc) return rc;
@@ -454,7 +538,16 @@ int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t b
   }
   PrefillParams p;
   int64_t nb = 0;
-  if ((rc = build_prefill(L, batch, num_tokens, start_pos, &p, &nb))) return rc;
+  if ((rc = build_prefill(L, batch, num_tokens, start_pos, workspace != nullptr, &p, &nb))) return rc;
+  const PrefillWs wl = prefill_ws_layout(p);
+  if (workspace != nullptr) {
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(DUO_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (workspace_bytes < wl.total)
+      return fail(DUO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", wl.total, workspace_bytes);
+    p.ws_count = static_cast<int32_t*>(workspace);
+    p.ws_part = reinterpret_cast<float*>(static_cast<char*>(workspace) + wl.part);
+  }
   if ((rc = read_epilogue(epilogue, &p.sink_logits, &p.gate, &p.gate_mode))) return rc;
   if ((rc = read_prologue(q_prologue, &p.qpro, &p.qpro_on))) return rc;
   p.q = static_cast<const uint16_t*>(q);

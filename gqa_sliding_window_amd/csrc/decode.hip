@@ -199,22 +199,6 @@ __device__ __forceinline__ void attend_tile(const uint16_t* sK, const uint16_t* 
   __builtin_amdgcn_s_setprio(0);
 }
 
-// Device-coherent (sc1) store / load: visible across XCDs without flushing
-// the L2 caches.
-__device__ __forceinline__ void coherent_store(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float coherent_load(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-// Two consecutive floats (8-byte aligned) in one device-coherent load.
-__device__ __forceinline__ f32x2 coherent_load2(const float* p) {
-  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  return __builtin_bit_cast(f32x2, v);
-}
-
 // Output values (dim, dim + 1) of row bh: the unnormalised pair times the
 // row's normaliser and, if the call has one, the output gate.
 template <bool kFused>

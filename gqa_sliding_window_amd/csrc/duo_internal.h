@@ -17,6 +17,19 @@ constexpr int kMaxGroup = 16;     // query heads per KV head (MFMA columns)
 #endif
 constexpr int kPrefillRows = DUO_PREFILL_ROWS;  // query rows per prefill workgroup
 constexpr int kPrefillKeys = 64;  // keys per prefill K/V tile
+// Prefill key-range split: resident prefill workgroups on an MI355X (256 CUs,
+// two 4-wave workgroups per CU), the most pieces one unit's keys are cut into,
+// the fewest key tiles a piece gets, and the extra cost of a piece (its own
+// query load and start-up, its partial write and the merge) in tile-steps.
+constexpr int kPrefillSlots = 512;
+constexpr int kMaxPieces = 8;
+constexpr int kMinPieceTiles = 8;
+constexpr int kPieceCost = 4;
+// One piece's partial result: [4 waves][2 column blocks][8 dim blocks][64
+// lanes] float4 (the unnormalised output in the MFMA accumulator layout),
+// then [4 waves][2 column blocks][16 rows] (max, sum) float pairs.
+constexpr int kPartOutFloats = 4 * 2 * 8 * 64 * 4;
+constexpr int kPartFloats = kPartOutFloats + 4 * 2 * 16 * 2;
 constexpr int kDecodeKeys = 32;   // keys per decode tile (one wave)
 constexpr int kDecodeWaves = 4;   // waves per decode workgroup
 constexpr int kXcds = 8;          // MI355X: 8 XCDs, workgroups dispatched round-robin
@@ -136,6 +149,10 @@ struct PrefillParams {
   int32_t n_qtiles;
   int32_t n_units_main;  // (q tile, batch, main head) units
   int32_t n_units;       // all units
+  int32_t n_units_main8; // n_units_main rounded up to a multiple of kXcds
+  int32_t n_pieces;      // key-range pieces per main unit (1: no split)
+  int32_t* ws_count;     // [n_units_main, group] arrival counters, zero between calls
+  float* ws_part;        // [n_units_main, group, n_pieces] partial results (kPartFloats each)
   float scale_log2;      // scale * log2(e)
   const float* sink_logits;  // [Hq] attention-sink logits (natural units) or null
   const uint16_t* gate;      // bf16 output gate or null
@@ -148,30 +165,48 @@ struct PrefillItem {
   int32_t valid;
   int32_t cls;
   int32_t b, kvh, rank, qhead, qtile;
+  int32_t unit;   // index of the unit within its class
+  int32_t piece;  // key-range piece of a main unit (0 for streaming units)
 };
 
-// Workgroup -> work item. Units (one kPrefillRows-row query tile of one KV-head group)
-// are ordered main-class units before streaming units. Unit u runs on XCD
-// u % 8 (workgroups are dispatched to XCDs round-robin); the `group` query
-// heads of one unit are consecutive on that XCD and share the unit's K/V
-// tiles through its L2. When a class's (batch, KV head) groups fill whole
-// 8-wide stripes, each XCD takes its groups one at a time, later query tiles
-// first; otherwise all groups advance together, later query tiles first, so
-// every XCD gets an equal share of each cost level.
+// Workgroup -> work item. Units (one kPrefillRows-row query tile of one
+// KV-head group) are ordered main-class units before streaming units. A main
+// unit may be cut into n_pieces key-range pieces (long units of a chunked
+// prefill over a long past), each a workgroup of its own; its pieces are merged
+// by the last one to finish. Unit u runs on XCD u % 8 (workgroups are
+// dispatched to XCDs round-robin); the `group` query heads of one unit, and
+// its pieces, are consecutive on that XCD, so they share the unit's K/V tiles
+// through its L2. When a class's (batch, KV head) groups fill whole 8-wide
+// stripes, each XCD takes its groups one at a time, later query tiles first;
+// otherwise all groups advance together, later query tiles first, so every
+// XCD gets an equal share of each cost level. The main class is padded to a
+// multiple of 8 units (padding workgroups exit at once).
 // (32-bit arithmetic: the host keeps grids below 2^31 workgroups; a 64-bit
 // division would run as a long software sequence in every workgroup.)
 __host__ __device__ inline PrefillItem prefill_item(const PrefillParams& p, int block) {
   PrefillItem it{};
   const int x = block % kXcds;
   const int s = block / kXcds;
-  const int unit = (s / p.group) * kXcds + x;
+  const int vu = (s / p.group) * kXcds + x;  // virtual unit
   const int g = s % p.group;
-  if (unit >= p.n_units) { it.valid = 0; return it; }
+  const int main_v = p.n_units_main8 * p.n_pieces;
+  int u, n_class;
+  if (vu < main_v) {
+    const int j = vu / kXcds;
+    u = (j / p.n_pieces) * kXcds + x;
+    it.piece = j % p.n_pieces;
+    if (u >= p.n_units_main) { it.valid = 0; return it; }
+    it.cls = kMain;
+    n_class = p.n_main;
+  } else {
+    u = vu - main_v;
+    if (u >= p.n_units - p.n_units_main) { it.valid = 0; return it; }
+    it.piece = 0;
+    it.cls = kStream;
+    n_class = p.n_stream;
+  }
   it.valid = 1;
-  int u = unit;
-  int n_class = p.n_main;
-  it.cls = kMain;
-  if (u >= p.n_units_main) { u -= p.n_units_main; it.cls = kStream; n_class = p.n_stream; }
+  it.unit = u;
   const int groups = p.batch * n_class;
   int grp;
   if (groups % kXcds == 0) {
@@ -191,6 +226,20 @@ __host__ __device__ inline PrefillItem prefill_item(const PrefillParams& p, int 
   it.kvh = class_head(p.stream_mask, p.hkv, it.cls, it.rank);
   it.qhead = it.kvh * p.group + g;
   return it;
+}
+
+// Tiles [t0, t1) of piece `piece` of a unit with `ntiles` key tiles cut into
+// n_pieces pieces of ceil(ntiles / n_pieces) tiles; `used` is the number of
+// non-empty pieces (the later pieces of a short unit are empty).
+struct PieceRange { int t0, t1, used; };
+__host__ __device__ inline PieceRange piece_range(int ntiles, int n_pieces, int piece) {
+  const int per = (ntiles + n_pieces - 1) / n_pieces;
+  PieceRange r;
+  if (per == 0) { r.t0 = r.t1 = 0; r.used = 1; return r; }
+  r.t0 = piece * per < ntiles ? piece * per : ntiles;
+  r.t1 = r.t0 + per < ntiles ? r.t0 + per : ntiles;
+  r.used = (ntiles + per - 1) / per;
+  return r;
 }
 
 // Key ranges (absolute positions, inclusive) a work item must visit for its

@@ -87,6 +87,27 @@ __device__ __forceinline__ RowNorm row_norm(float M, float L, const float* sink_
 // Output gate (same post, attention output gating): each output value times
 // the logistic function of its gate value.
 __device__ __forceinline__ float gate_factor(float g) { return 1.f / (1.f + __expf(-g)); }
+// Device-coherent (sc1) stores and loads at agent scope: visible to a
+// workgroup on another XCD without writing back or invalidating the L2 caches.
+// They carry the split-K partial results between the workgroups of one launch.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Two consecutive floats (8-byte aligned) in one device-coherent store / load.
+__device__ __forceinline__ void coherent_store2(float* p, f32x2 v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x2 coherent_load2(const float* p) {
+  const uint64_t v = __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<float*>(p)), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return __builtin_bit_cast(f32x2, v);
+}
+
 // Lazy rescaling: the running row maximum is only moved when a new logit
 // exceeds it by more than this many powers of two; until then exponentials may
 // reach 2^8, far inside fp32 and bf16 range. Output and normaliser share the

@@ -193,6 +193,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
   __shared__ __attribute__((aligned(16))) uint16_t sK1[kPrefillKeys * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t sV1[kPrefillKeys * kVPitch];
 
+  __shared__ int s_last;
   const PrefillItem it = prefill_item(p, blockIdx.x);
   if (!it.valid) return;
 
@@ -240,6 +241,12 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
       ntiles += (int)tiles_of(k1);
     }
   }
+  // this workgroup's piece of the unit's tiles (a main unit may be cut into
+  // key-range pieces that are merged below; the later pieces of a short unit
+  // are empty)
+  const PieceRange pr = piece_range(ntiles, it.cls == kMain ? p.n_pieces : 1, it.piece);
+  if (pr.t0 >= pr.t1) return;
+  const int t_end = pr.t1;
 
   KvSrc src;
   src.cstride = (int64_t)p.hkv * kD;
@@ -333,7 +340,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
         }
       }
     }
-    if (idx + 1 < ntiles) issue(idx + 1, nK, nV);
+    if (idx + 1 < t_end) issue(idx + 1, nK, nV);
     __builtin_amdgcn_s_setprio(0);
     if (!invisible) {
       const bool need_mask = !(lo >= r.lo && hi <= r.hi && hi <= qw0 && (r.span == 0 || lo >= qw1 - r.span + 1));
@@ -416,13 +423,71 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
     __syncthreads();
   };
 
-  issue(0, sK0, sV0);
+  issue(pr.t0, sK0, sV0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int idx = 0; idx < ntiles; idx += 2) {
+  for (int idx = pr.t0; idx < t_end; idx += 2) {
     step(idx, sK0, sV0, sK1, sV1);
-    if (idx + 1 >= ntiles) break;
+    if (idx + 1 >= t_end) break;
     step(idx + 1, sK1, sV1, sK0, sV0);
+  }
+
+  // row sums: the 4 lanes of a row each hold the sum over their own keys
+#pragma unroll
+  for (int t = 0; t < kRT; ++t) {
+    l[t] += __shfl_xor(l[t], 16);
+    l[t] += __shfl_xor(l[t], 32);
+  }
+
+  // ---- key-range pieces: every piece publishes its partial (running max,
+  // sum and unnormalised output, in the accumulator layout) with
+  // device-coherent stores, waits for them to complete, and bumps the unit's
+  // arrival counter; the last piece to arrive reads all partials back, its
+  // own included, and combines them in piece order (max, rescale, add), so
+  // the result does not depend on which piece finished last; it finishes the
+  // rows below and resets the counter for the next call.
+  if (pr.used > 1) {
+    const int64_t cslot = (int64_t)it.unit * p.group + (it.qhead - it.kvh * p.group);
+    const float* parts = p.ws_part + cslot * p.n_pieces * kPartFloats;
+    float* mine = p.ws_part + (cslot * p.n_pieces + it.piece) * kPartFloats;
+#pragma unroll
+    for (int t = 0; t < kRT; ++t) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+        float* dst = mine + (((wave * kRT + t) * 8 + dt) * 64 + lane) * 4;
+        coherent_store2(dst, f32x2{o[t][dt][0], o[t][dt][1]});
+        coherent_store2(dst + 2, f32x2{o[t][dt][2], o[t][dt][3]});
+      }
+      if (g == 0) coherent_store2(mine + kPartOutFloats + ((wave * kRT + t) * 16 + r16) * 2, f32x2{m[t], l[t]});
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    int32_t* counter = p.ws_count + cslot;
+    if (tid == 0)
+      s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == pr.used - 1);
+    __syncthreads();
+    if (!s_last) return;
+    for (int q = 0; q < pr.used; ++q) {
+      const float* src = parts + (int64_t)q * kPartFloats;
+#pragma unroll
+      for (int t = 0; t < kRT; ++t) {
+        const f32x2 ml = coherent_load2(src + kPartOutFloats + ((wave * kRT + t) * 16 + r16) * 2);
+        const float mx = q == 0 ? ml.x : fmaxf(m[t], ml.x);
+        const float a = (q == 0 || m[t] == kNegInf) ? 0.f : fast_exp2(m[t] - mx);
+        const float b = (ml.x == kNegInf) ? 0.f : (q == 0 ? 1.f : fast_exp2(ml.x - mx));
+        m[t] = mx;
+        l[t] = (q == 0 ? 0.f : l[t] * a) + ml.y * b;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+          const float* ps = src + (((wave * kRT + t) * 8 + dt) * 64 + lane) * 4;
+          const f32x2 lo = coherent_load2(ps);
+          const f32x2 hi = coherent_load2(ps + 2);
+          const f32x4 po = f32x4{lo.x, lo.y, hi.x, hi.y};
+          o[t][dt] = q == 0 ? po : o[t][dt] * a + po * b;
+        }
+      }
+    }
+    if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   if (!wave_active) return;
@@ -430,9 +495,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
   // the output gate, bf16 round-to-nearest-even; lse = (m + log2 l) ln 2
 #pragma unroll
   for (int t = 0; t < kRT; ++t) {
-    float lt = l[t];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = l[t];
     const int qpos = qw0 + 16 * t + r16;
     if (qpos > qb) continue;
     float inv = 1.f / lt;

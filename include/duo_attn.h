@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define DUO_ATTN_VERSION 1
+#define DUO_ATTN_VERSION 2
 #define DUO_HEAD_DIM 128
 #define DUO_MAX_KV_HEADS 32
 #define DUO_MAX_GROUP 16
@@ -71,7 +71,7 @@ typedef enum duo_status {
   DUO_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size or range   */
   DUO_ERR_UNSUPPORTED = -2,  /* head_dim != 128, group > 16, kv heads > 32     */
   DUO_ERR_CAPACITY = -3,     /* positions beyond the caller's cache capacity  */
-  DUO_ERR_WORKSPACE = -4,    /* decode workspace missing or too small         */
+  DUO_ERR_WORKSPACE = -4,    /* workspace missing, too small or misaligned    */
   DUO_ERR_HIP = -5           /* a HIP launch failed                          */
 } duo_status;
 
@@ -189,6 +189,12 @@ typedef struct duo_epilogue {
 } duo_epilogue;
 
 /* Write new K/V rows into the cache (the streaming-head cache manager).
+ * Defined by the model card "DuoAttention Laguna Adapter": "Summary" (KV heads
+ * are full-context or streaming; a streaming head keeps the 64 sink and the
+ * 256 most recent positions) and "Changes In This Submission" (a static Duo
+ * KV cache, heads reordered so that the two classes are stored apart). The
+ * slot of each position is the library's reading of those passages (the
+ * pages never describe slots): see duo_kv_cache.
  * k_new, v_new : device [batch, num_tokens, Hkv, 128] (token-major, as the
  *                projections emit them); token t of sequence b is position
  *                start_pos[b] + t.
@@ -209,6 +215,13 @@ int duo_kv_append(const duo_layer* layer, const duo_kv_cache* cache, int32_t bat
 
 /* Prefill attention for a chunk of num_tokens query positions
  * [start_pos, start_pos + num_tokens) of every sequence in the batch.
+ * Defined by the blog post on Laguna-M.1-8bit attention, sliding-window
+ * section (each token attends a fixed-width window of earlier tokens) and
+ * mask-generation section (a causal or a sliding-window causal mask per layer
+ * type), and by the model card "DuoAttention Laguna Adapter", "Why It Works"
+ * (full-context heads see every earlier position, streaming heads only the
+ * sink and the most recent ones). The visibility rules at the top of this
+ * file restate them; the result is the exact masked softmax.
  * q   : device [batch, num_tokens, Hq, 128]
  * k,v : device [batch, num_tokens, Hkv, 128] -- the chunk's own keys/values.
  * past: the cache holding positions [0, start_pos) as duo_kv_append left it;
@@ -222,14 +235,38 @@ int duo_kv_append(const duo_layer* layer, const duo_kv_cache* cache, int32_t bat
  *       must already hold the prologue's output (duo_qk_prologue).
  * epilogue : NULL or the attention sink / output gate (duo_epilogue); a
  *       per-element gate is [batch, num_tokens, Hq, 128], a per-head gate
- *       [batch, num_tokens, Hq]. */
+ *       [batch, num_tokens, Hq].
+ * workspace : NULL, or device scratch of at least
+ *       duo_attn_prefill_workspace_bytes() bytes (256-byte aligned, caller
+ *       owned, zero-filled once before its first use with
+ *       duo_attn_decode_workspace_init or any zero fill; every completed call
+ *       leaves its counters at zero again). With a workspace, the full-context
+ *       query tiles of a chunk over a long past are cut into key-range pieces
+ *       that run as separate workgroups and are merged in the same launch
+ *       (partial max, sum and output, as the decode's split-K), so the longest
+ *       work items no longer set the launch's length; the size is 0 (and the
+ *       workspace unused) when no piece would be cut. Without one, every query
+ *       tile runs whole. The result is the same either way up to fp32
+ *       summation order. A workspace smaller than needed, or misaligned, is
+ *       DUO_ERR_WORKSPACE. Calls that share a workspace must be ordered. */
 int duo_attn_prefill(const duo_layer* layer, const duo_kv_cache* past, int32_t batch,
                      const void* q, const void* k, const void* v, int32_t num_tokens,
-                     int64_t start_pos, void* out, float* lse, const duo_prologue* q_prologue,
+                     int64_t start_pos, void* out, float* lse, void* workspace,
+                     size_t workspace_bytes, const duo_prologue* q_prologue,
                      const duo_epilogue* epilogue, void* stream);
+
+/* Workspace size for duo_attn_prefill at these sizes (0 when the call would
+ * cut no query tile into pieces, and on invalid arguments). Host only. */
+size_t duo_attn_prefill_workspace_bytes(const duo_layer* layer, int32_t batch, int32_t num_tokens,
+                                        int64_t start_pos);
 
 /* Decode attention: one query token per sequence at position seq_lens[b]-1,
  * whose K/V have already been appended (seq_lens counts them).
+ * Defined by the same passages as duo_attn_prefill (Laguna-M.1-8bit post,
+ * sliding-window and mask-generation sections; model card "DuoAttention
+ * Laguna Adapter", "Why It Works"), applied to the newest token: the
+ * decode-time KV reads that the model card's "Benefits" section says the
+ * streaming heads shrink.
  * q         : device [batch, Hq, 128]
  * seq_lens  : device int32 [batch], each in [1, max_seq_len]; a 0 entry
  *             yields a zero output row (lse = -inf, or the sink logit when
@@ -283,8 +320,8 @@ int duo_attn_decode_block(const duo_layer* layer, const duo_kv_cache* cache, int
 size_t duo_attn_decode_block_workspace_bytes(const duo_layer* layer, int32_t batch,
                                              int32_t num_tokens, int64_t max_past_len);
 
-/* Zero-fill a decode workspace (enqueued on `stream`; a small fill kernel, so
- * it is also safe under graph capture). */
+/* Zero-fill a decode or prefill workspace (enqueued on `stream`; a small fill
+ * kernel, so it is also safe under graph capture). */
 int duo_attn_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host only: the angular frequency f_i (radians per position) of each of the
@@ -339,12 +376,15 @@ int duo_head_plan(const duo_layer* layer, int32_t* head_class, int32_t* head_ran
                   int32_t* n_main, int32_t* n_stream);
 
 /* Prefill work plan (host only): the number of workgroups the prefill launch
- * uses; when `items` is not NULL it receives, per workgroup, four int32
- * (batch, q_head, q_tile, key_tiles), or (-1, -1, -1, 0) for padding, with
- * q_tile a duo_prefill_tile_rows()-row tile of the chunk and key_tiles the 64-key tiles the
- * workgroup visits after masked tiles are skipped. */
+ * uses, with a workspace (with_workspace != 0) or without one; when `items`
+ * is not NULL it receives, per workgroup, six int32 (batch, q_head, q_tile,
+ * key_tiles, piece, pieces), or (-1, -1, -1, 0, 0, 0) for padding, with q_tile
+ * a duo_prefill_tile_rows()-row tile of the chunk, key_tiles the 64-key tiles
+ * the workgroup visits after masked tiles are skipped, and piece / pieces its
+ * key-range piece and the number of non-empty pieces of its query tile (1
+ * when the tile runs whole; a workgroup with key_tiles 0 is an empty piece). */
 int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens,
-                     int64_t start_pos, int32_t* items, int64_t* n_items);
+                     int64_t start_pos, int32_t with_workspace, int32_t* items, int64_t* n_items);
 
 /* Query rows per prefill work item (the q_tile unit of duo_prefill_plan). */
 int duo_prefill_tile_rows(void);

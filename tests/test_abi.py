@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(lib):
     raw = ctypes.CDLL(g.LIB_PATH)
     for n in names:
         assert hasattr(raw, n), n
-    assert lib.load().duo_attn_version() == 1
+    assert lib.load().duo_attn_version() == 2
 
 
 def _err(fn, *a, **k):
@@ -173,9 +173,10 @@ def test_prefill_plan_covers_every_tile_once_and_skips_masked(lib, case):
     nqt = (T + rows - 1) // rows
     assert len(real) == B * L.num_q_heads * nqt
     assert len({tuple(r[:3]) for r in real}) == len(real)
+    assert (real[:, 4] == 0).all() and (real[:, 5] == 1).all()  # no pieces without a workspace
     G = L.num_q_heads // L.num_kv_heads
     mask = L.full_attention_heads
-    for b, h, qt, nt in real:
+    for b, h, qt, nt, _, _ in real:
         qa = P + rows * qt
         qb = min(qa + rows - 1, P + T - 1)
         streaming = mask is not None and mask[h // G] == 0
@@ -203,6 +204,53 @@ def test_prefill_plan_covers_every_tile_once_and_skips_masked(lib, case):
             assert all(a >= b for a, b in zip(nts, nts[1:]))
 
 
+@pytest.mark.parametrize("case", [
+    dict(layer=Layer(full_attention_heads=[0, 0, 0, 0, 1, 0, 1, 0]), B=1, T=8192, P=8192 * 15),
+    dict(layer=Layer(full_attention_heads=[0, 0, 0, 0, 1, 0, 1, 0]), B=1, T=8192, P=0),
+    dict(layer=Layer(full_attention_heads=[1, 0, 0, 0, 0, 0, 0, 0]), B=1, T=1000, P=40000),
+    dict(layer=Layer(num_q_heads=12, num_kv_heads=2), B=1, T=333, P=70000),
+])
+def test_prefill_plan_pieces_cover_each_query_tile_once(lib, case):
+    """With a workspace, long full-context query tiles are cut into key-range
+    pieces: the pieces of a (batch, head, query tile) are numbered 0..pieces-1
+    and their key tiles add up to the tile's visible key tiles; streaming
+    heads are never cut; the workspace covers every piece's partial."""
+    L, B, T, P = case["layer"], case["B"], case["T"], case["P"]
+    items = g.prefill_plan(L, B, T, P, with_workspace=True)
+    real = items[items[:, 0] >= 0]
+    rows = g.prefill_tile_rows()
+    G = L.num_q_heads // L.num_kv_heads
+    mask = L.full_attention_heads
+    by_tile = {}
+    for b, h, qt, nt, piece, pieces in real:
+        by_tile.setdefault((b, h, qt), []).append((piece, pieces, nt))
+    nqt = (T + rows - 1) // rows
+    assert len(by_tile) == B * L.num_q_heads * nqt
+    cut = 0
+    for (b, h, qt), ps in by_tile.items():
+        qa = P + rows * qt
+        qb = min(qa + rows - 1, P + T - 1)
+        streaming = mask is not None and mask[h // G] == 0
+        used = {p[1] for p in ps}
+        assert len(used) == 1
+        used = used.pop()
+        nonempty = sorted(p[0] for p in ps if p[2] > 0)
+        assert nonempty == list(range(used))
+        assert sum(p[2] for p in ps) == _expected_tiles(L, qa, qb, streaming)
+        if streaming:
+            assert used == 1
+        cut += used > 1
+    nbytes = g.prefill_workspace_bytes(L, B, T, P)
+    if cut:
+        n_pieces = max(p[0] for ps in by_tile.values() for p in ps) + 1
+        n_main_tiles = B * L.n_main * nqt * G
+        assert nbytes >= n_main_tiles * n_pieces * (4 * 2 * 8 * 64 * 4 + 4 * 2 * 16 * 2) * 4
+    else:
+        assert nbytes == 0
+    if P == 8192 * 15:
+        assert cut  # the long chunk is cut
+
+
 def test_decode_plan(lib):
     sk, items = g.decode_plan(Layer(kind=SLIDING, window=512), 64, 32768)
     assert sk >= 128 and sk % 32 == 0
@@ -217,10 +265,19 @@ def test_decode_plan(lib):
     assert (items[:, 3][:len(full)] == 0).all()   # main-class (long) items come first
 
 
-def test_visible_pairs_closed_forms():
+def test_visible_pairs_closed_forms(lib):
+    """bench.py's algorithmic FLOP count against the figures derived by hand
+    for the 1 x 1024 sliding prefill and the 4 x 8192 full prefill, and
+    against a direct sum of |Vis(i)| for a chunk of a Duo layer."""
+    import bench
     L = Layer(kind=SLIDING, window=512, num_q_heads=12, num_kv_heads=2)
-    assert g.prefill_flops(L, 1, 1024) == 2417491968
-    assert g.prefill_flops(Layer(), 4, 8192) == 3298937536512
+    assert bench.prefill_flops(g, L, 1, 1024) == 2417491968
+    assert bench.prefill_flops(g, Layer(), 4, 8192) == 3298937536512
+    D = Layer(full_attention_heads=[1, 0, 0, 0, 0, 0, 0, 1])
+    direct = 0
+    for i in range(300, 300 + 700):
+        direct += 2 * (i + 1) * 6 + 6 * 6 * min(i + 1, 64 + 256)
+    assert bench.prefill_flops(g, D, 1, 700, 300) == 4 * 128 * direct
 
 
 def test_epilogue_validation_errors(lib):
@@ -238,7 +295,8 @@ def test_epilogue_validation_errors(lib):
     for sl, gate, mode in ((0, 0, 1), (0, 0x800000, 0), (0, 0x800000, 3)):
         e = g._Epilogue(sl, gate, mode)
         rc = lib.load().duo_attn_prefill(ctypes.byref(Layer()._c()), None, 1, q.data_ptr(), kv.data_ptr(),
-                                         kv.data_ptr(), 8, 0, o.data_ptr(), None, None, ctypes.byref(e), None)
+                                         kv.data_ptr(), 8, 0, o.data_ptr(), None, None, 0, None,
+                                         ctypes.byref(e), None)
         assert rc == -1, (sl, gate, mode)
         assert "gate" in lib.load().duo_last_error().decode()
     # decode and block decode check the epilogue too
@@ -340,3 +398,45 @@ def test_binding_rejects_misshaped_tensors():
         g.kv_append(L, FakeCache(), kv, kv, torch.zeros(0, dtype=torch.int32), max_end_pos=16, stream=0)
     with pytest.raises(ValueError, match="norm_weight"):
         g.qk_prologue(g.Prologue(norm_weight=torch.zeros(64)), q, torch.zeros(1, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("other", [
+    dict(full_attention_heads=[1, 1, 0, 0, 0, 0, 0, 0]),          # another class split
+    dict(full_attention_heads=[0, 1, 0, 0, 0, 0, 0, 0]),          # same counts, other heads
+    dict(full_attention_heads=[1, 0, 0, 0, 0, 0, 0, 0], sink=32),  # shorter sink + recent ring
+    dict(full_attention_heads=[1, 0, 0, 0, 0, 0, 0, 0], recent=128),
+    dict(kind=SLIDING, window=512),                               # a ring where a full cache was built
+    dict(),                                                       # no Duo routing: every head full
+])
+def test_binding_rejects_a_cache_built_for_another_layer(lib, other):
+    """A KVCache keeps its layer: a call with a layer of other head classes,
+    sink/recent or window is refused before the C ABI, which only sees the
+    cache's pointers and would read and write past its tensors."""
+    import torch
+    built = Layer(full_attention_heads=[1, 0, 0, 0, 0, 0, 0, 0])
+    cache = g.KVCache(built, 2, 64, device="cpu")
+    call = Layer(**other)
+    kv = torch.zeros(2, 4, 8, 128, dtype=torch.bfloat16)
+    sp = torch.zeros(2, dtype=torch.int32)
+    with pytest.raises(ValueError, match="another layer geometry"):
+        g.kv_append(call, cache, kv, kv, sp, max_end_pos=4, stream=0)
+    q = torch.zeros(2, 48, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="another layer geometry"):
+        g.attn_decode(call, cache, q, sp, 16, q, torch.zeros(64), stream=0)
+    qp = torch.zeros(2, 4, 48, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="another layer geometry"):
+        g.attn_prefill(call, qp, kv, kv, qp, start_pos=8, past=cache, stream=0)
+    # the layer it was built for passes the cache checks (and stops at the
+    # device check: these are host tensors)
+    with pytest.raises(ValueError, match="device memory"):
+        g.kv_append(built, cache, kv, kv, sp, max_end_pos=4, stream=0)
+
+
+def test_binding_rejects_a_resized_cache_tensor(lib):
+    import torch
+    L = Layer(full_attention_heads=[1, 0, 0, 0, 0, 0, 0, 0])
+    cache = g.KVCache(L, 1, 64, device="cpu")
+    cache.k_stream = torch.zeros(1, 7, 100, 128, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 4, 8, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="k_stream"):
+        g.kv_append(L, cache, kv, kv, torch.zeros(1, dtype=torch.int32), max_end_pos=4, stream=0)

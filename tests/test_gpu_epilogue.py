@@ -59,6 +59,10 @@ PREFILL_CASES = {
                                       True, "head"),
     "sliding_w64_sink_only": (dict(kind=1, window=64, num_q_heads=8, num_kv_heads=2), 1, 300, 0, True, None),
     "full_gate_elem_only": (dict(num_q_heads=16, num_kv_heads=2), 1, 200, 0, False, "elem"),
+    # a prefill workspace: the full-context query tiles cut into key-range
+    # pieces, merged before the sink and the gate are applied
+    "full_duo_long_chunk_sink_gate_elem_pieces": (dict(full_attention_heads=[1, 0, 0, 1, 0, 0, 0, 0]), 1, 640,
+                                                  2048, True, "elem"),
 }
 
 
@@ -81,9 +85,13 @@ def test_prefill_epilogue(lib, name):
     sl, gbits, _ = _epilogue_inputs(seed, (B, T), hq, sink, gate)
     out = torch.empty((B, T, hq, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, hq, T), dtype=torch.float32, device="cuda")
+    ws = None
+    if name.endswith("_pieces"):
+        ws = lib.prefill_workspace(layer, B, T, [P])
+        assert lib.prefill_plan(layer, B, T, P, True)[:, 5].max() > 1, "no query tile was cut"
     lib.attn_prefill(layer, dev(q), dev(k[:, P:]), dev(v[:, P:]), out, start_pos=P, past=past, lse=lse,
                      sink_logits=None if sl is None else torch.from_numpy(sl).cuda(),
-                     gate=None if gbits is None else dev(gbits))
+                     gate=None if gbits is None else dev(gbits), workspace=ws)
     torch.cuda.synchronize()
     ob, lg = host_bits(out), lse.cpu().numpy()
     rows = np.array([(b, h, t) for b in range(B) for h in range(hq) for t in range(T)], dtype=np.int64)

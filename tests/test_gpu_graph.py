@@ -52,16 +52,30 @@ def test_decode_step_graph_replays_match_eager(lib):
     outb = torch.empty((B, T, hq, 128), dtype=torch.bfloat16, device="cuda")
     outc = torch.empty((1, 256, hq, 128), dtype=torch.bfloat16, device="cuda")
     lc = lib.Layer(kind=lib.SLIDING, window=512)
+    # a chunk over the Duo cache's longest sequence with a prefill workspace:
+    # its full-context query tiles are cut into pieces merged in the launch
+    # (arrival counters return to zero inside each replay)
+    P = lengths[2]
+    qp = dev(wl.normal_tokens(45, wl.Q, 1, P, 256, hq, 128))
+    kp = dev(wl.normal_tokens(45, wl.K, 1, P, 256, hkv, 128))
+    vp = dev(wl.normal_tokens(45, wl.V, 1, P, 256, hkv, 128))
+    outp = torch.empty((1, 256, hq, 128), dtype=torch.bfloat16, device="cuda")
+    wsp = lib.prefill_workspace(layer, 1, 256, [P])
+    assert lib.prefill_plan(layer, 1, 256, P, True)[:, 5].max() > 1, "no query tile was cut"
+    past2 = lib.KVCache(layer, 1, cap)
+    past2.k_main, past2.v_main = cache.k_main[2:3], cache.v_main[2:3]
+    past2.k_stream, past2.v_stream = cache.k_stream[2:3], cache.v_stream[2:3]
 
     def step():
         lib.kv_append(layer, cache, kn, vn, pos, max_end_pos=maxlen, k_prologue=pro)
         lib.attn_decode(layer, cache, q1, seq, maxlen, out, ws, lse=lse, q_prologue=pro, sink_logits=sink)
         lib.attn_decode_block(layer, cache, qb, kb, vb, seq, maxlen, outb, wsb, sink_logits=sink)
         lib.attn_prefill(lc, qc, kc, vc, outc)
+        lib.attn_prefill(layer, qp, kp, vp, outp, start_pos=P, past=past2, workspace=wsp)
 
     step()
     torch.cuda.synchronize()
-    want = [host_bits(out), lse.cpu().numpy().copy(), host_bits(outb), host_bits(outc)]
+    want = [host_bits(out), lse.cpu().numpy().copy(), host_bits(outb), host_bits(outc), host_bits(outp)]
 
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -76,9 +90,10 @@ def test_decode_step_graph_replays_match_eager(lib):
         out.zero_()
         outb.zero_()
         outc.zero_()
+        outp.zero_()
         g.replay()
         torch.cuda.synchronize()
-        got = [host_bits(out), lse.cpu().numpy(), host_bits(outb), host_bits(outc)]
-        for name, a, b_ in zip(("decode", "lse", "block", "prefill"), got, want):
+        got = [host_bits(out), lse.cpu().numpy(), host_bits(outb), host_bits(outc), host_bits(outp)]
+        for name, a, b_ in zip(("decode", "lse", "block", "prefill", "prefill pieces"), got, want):
             assert np.array_equal(a, b_), f"replay {r}: {name} differs from the eager result"
         torch.ones(1024, device="cuda").sum().item()   # eager work between replays

@@ -85,6 +85,36 @@ def test_prefill_chunks_and_append_stay_inside(lib):
         assert_bands(bands, f"append at {P}")
 
 
+def test_prefill_pieces_stay_inside(lib):
+    """A Duo chunk over a 3000-token past with a prefill workspace (its
+    full-context query tiles cut into key-range pieces, a ragged last tile):
+    out, lse, the workspace and the cache it reads; twice on one workspace."""
+    import torch
+    announce("guard bands: prefill pieces")
+    layer = lib.Layer(full_attention_heads=[0, 1, 0, 0, 0, 0, 0, 1])
+    B, P, T = 2, 3000, 300
+    hq, hkv = layer.num_q_heads, layer.num_kv_heads
+    q = wl.normal_tokens(76, wl.Q, B, P, T, hq, 128)
+    k = wl.normal_tokens(76, wl.K, B, 0, P + T, hkv, 128)
+    v = wl.normal_tokens(76, wl.V, B, 0, P + T, hkv, 128)
+    cache, bands = guarded_cache(lib, layer, B, P + T)
+    sp = torch.zeros(B, dtype=torch.int32, device="cuda")
+    lib.kv_append(layer, cache, dev(k[:, :P]), dev(v[:, :P]), sp, max_end_pos=P)
+    assert lib.prefill_plan(layer, B, T, P, True)[:, 5].max() > 1, "no query tile was cut"
+    nws = (lib.prefill_workspace_bytes(layer, B, T, P) + 3) // 4
+    ws = Guarded((nws,), torch.float32)
+    lib.init_decode_workspace(ws.t)
+    out = Guarded((B, T, hq, 128), torch.bfloat16)
+    lse = Guarded((B, hq, T), torch.float32)
+    for _ in range(2):
+        lib.attn_prefill(layer, dev(q), dev(k[:, P:]), dev(v[:, P:]), out.t, start_pos=P, past=cache,
+                         lse=lse.t, workspace=ws.t)
+    torch.cuda.synchronize()
+    assert out.margins_intact() and lse.margins_intact() and ws.margins_intact(), "prefill wrote outside"
+    assert out.fully_written() and lse.fully_written(), "prefill left an output element unwritten"
+    assert_bands(bands, "prefill pieces")
+
+
 def test_decode_stays_inside(lib):
     """Sliding layer with wrapped rings and a Duo layer with multi-split
     sequences: out, lse, workspace and caches."""

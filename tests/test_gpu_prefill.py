@@ -36,20 +36,27 @@ def _layer_kw(layer):
                 full_attention_heads=layer.full_attention_heads, scale=layer.scale)
 
 
-def run_chunked(lib, layer, q, k, v, chunk, want_lse=True):
+def run_chunked(lib, layer, q, k, v, chunk, want_lse=True, pieces=False):
     """Prefill [0, N) in chunks (attend, then append). Returns out bits
-    [B, N, Hq, D] and lse [B, Hq, N]."""
+    [B, N, Hq, D] and lse [B, Hq, N]. pieces: pass a prefill workspace, so
+    that long query tiles are cut into key-range pieces."""
     import torch
     B, N, hq, _ = q.shape
     cache = lib.KVCache(layer, B, N) if chunk < N else None
     out = torch.empty((B, N, hq, 128), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((B, hq, N), dtype=torch.float32, device="cuda") if want_lse else None
-    for P in range(0, N, chunk):
+    starts = list(range(0, N, chunk))
+    ws = lib.prefill_workspace(layer, B, chunk, starts) if pieces else None
+    if pieces:
+        cut = [int(lib.prefill_plan(layer, B, min(chunk, N - P), P, True)[:, 5].max()) for P in starts]
+        announce(f"prefill pieces per chunk {cut}")
+        assert max(cut) > 1, "no query tile was cut: the case does not exercise pieces"
+    for P in starts:
         T = min(chunk, N - P)
         qd, kd, vd = dev(q[:, P:P + T]), dev(k[:, P:P + T]), dev(v[:, P:P + T])
         od = torch.empty((B, T, hq, 128), dtype=torch.bfloat16, device="cuda")
         ld = torch.empty((B, hq, T), dtype=torch.float32, device="cuda") if want_lse else None
-        lib.attn_prefill(layer, qd, kd, vd, od, start_pos=P, past=cache, lse=ld)
+        lib.attn_prefill(layer, qd, kd, vd, od, start_pos=P, past=cache, lse=ld, workspace=ws)
         out[:, P:P + T] = od
         if want_lse:
             lse[:, :, P:P + T] = ld
@@ -157,6 +164,35 @@ def test_prefill_parity_all_rows(lib, name):
     compare_rows(layer, q, k, v, out, lse, all_rows(B, N, layer.num_q_heads), name)
 
 
+# key-range pieces (a prefill workspace): 2 to 5 pieces per long query tile,
+# ragged chunk and tile edges, every row against the oracle
+PIECES = {
+    "duo_by_512_pieces": (dict(full_attention_heads=[0, 1], num_q_heads=12, num_kv_heads=2), 1, 2048, 512, 41),
+    "duo_ragged_by_333_pieces": (dict(full_attention_heads=[1, 0, 0, 0], num_q_heads=24, num_kv_heads=4),
+                                 2, 1600, 333, 42),
+    "full_by_1000_pieces": (dict(num_q_heads=6, num_kv_heads=1), 1, 2500, 1000, 43),
+}
+
+
+@pytest.mark.parametrize("name", list(PIECES))
+def test_prefill_pieces_parity_all_rows(lib, name):
+    kw, B, N, chunk, seed = PIECES[name]
+    announce(f"prefill parity {name}")
+    layer = lib.Layer(**kw)
+    q, k, v = _gen(seed, B, N, layer.num_q_heads, layer.num_kv_heads)
+    out, lse = run_chunked(lib, layer, q, k, v, chunk, pieces=True)
+    compare_rows(layer, q, k, v, out, lse, all_rows(B, N, layer.num_q_heads), name)
+    # the same chunks without a workspace (every tile whole): equal up to the
+    # rounding of the merge, and a second call on the same workspace repeats
+    # the first bit for bit (its counters were left at zero)
+    whole, lse_w = run_chunked(lib, layer, q, k, v, chunk)
+    diff = np.abs(bits_to_f64(out) - bits_to_f64(whole))
+    assert diff.max() <= 1.6e-2 and diff.mean() <= 1e-4, (diff.max(), diff.mean())
+    assert np.abs(lse - lse_w).max() < 1e-4
+    again, _ = run_chunked(lib, layer, q, k, v, chunk, pieces=True)
+    assert np.array_equal(again, out)
+
+
 def test_chunked_equals_one_shot(lib):
     announce("prefill chunked == one-shot")
     layer = lib.Layer(full_attention_heads=[0, 1, 0, 0, 0, 0, 1, 0])
@@ -196,14 +232,16 @@ def test_sliding_prefill_headline_shape_sampled(lib):
 def test_duo_chunked_prefill_workload_sampled(lib):
     """DuoAttention long-context chunked prefill at full size: batch 1, 131072
     tokens in 16 chunks of 8192 (attend, then append), 48/8 heads, the seeded
-    Bernoulli(0.25) head mask; 4096 seeded rows including the first and last
-    row of every chunk and the sink / recent edges."""
+    Bernoulli(0.25) head mask, with a prefill workspace (the full-context
+    query tiles cut into key-range pieces, as bench.py runs it); 4096 seeded
+    rows including the first and last row of every chunk and the sink /
+    recent edges."""
     w = wl.WORKLOADS[5]
     mask = wl.duo_mask(w).tolist()
     announce(f"prefill parity {w.name} mask {mask}")
     layer = lib.Layer(full_attention_heads=mask)
     q, k, v = _gen(w.seed, w.batch, w.seq, w.hq, w.hkv)
-    out, lse = run_chunked(lib, layer, q, k, v, w.chunk)
+    out, lse = run_chunked(lib, layer, q, k, v, w.chunk, pieces=True)  # as bench.py runs it
     rows = wl.sample_query_rows(w, w.seq, w.oracle_rows, chunk=w.chunk,
                                 must=(63, 64, 255, 256, 319, 320, 321, 8191 + 320, w.seq - 1))
     G = w.hq // w.hkv
