@@ -368,7 +368,7 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-ORACLE_ROWS = 1 << 18  # sample of the headline workload drawn for the oracle baseline
+ORACLE_ROWS = 1 << 19  # sample of the headline workload drawn for the oracle baseline
 
 
 def oracle_worker(idx: int, nproc: int, target_s: float):

@@ -231,6 +231,12 @@ def _cache_geometry(layer: "Layer"):
             "window": layer.window if layer.main_ring else 0, "sink": layer.sink, "recent": layer.recent}
 
 
+def _layer_key(layer: "Layer"):
+    mask = None if layer.full_attention_heads is None else tuple(int(x) for x in layer.full_attention_heads)
+    return (layer.num_q_heads, layer.num_kv_heads, layer.head_dim, layer.kind, layer.window, layer.sink,
+            layer.recent, mask)
+
+
 def _need_cache(cache, layer: "Layer", batch: int, batch_offset: int = 0):
     """A KVCache used by a call must cover its batch rows and have been built
     for a layer with the same head classes and sizes: the C ABI receives bare
@@ -240,6 +246,11 @@ def _need_cache(cache, layer: "Layer", batch: int, batch_offset: int = 0):
         return
     if batch_offset < 0 or batch_offset + batch > cache.batch:
         raise ValueError(f"cache holds {cache.batch} sequences; the call uses [{batch_offset}, {batch_offset + batch})")
+    # checked once per (layer, cache tensors): the per-call cost stays far
+    # below a decode kernel's
+    key = (_layer_key(layer), id(cache.k_main), id(cache.v_main), id(cache.k_stream), id(cache.v_stream))
+    if key in cache._checked:
+        return
     want, have = _cache_geometry(layer), _cache_geometry(cache.layer)
     diff = [k for k in want if want[k] != have[k]]
     if diff:
@@ -254,6 +265,7 @@ def _need_cache(cache, layer: "Layer", batch: int, batch_offset: int = 0):
             continue
         if t is None or tuple(t.shape) != shape or not t.is_contiguous():
             raise ValueError(f"cache.{name}: {None if t is None else tuple(t.shape)}, expected {shape} contiguous")
+    cache._checked.add(key)
 
 
 def _need_prologue(pro, name: str):
@@ -276,6 +288,7 @@ class KVCache:
         import torch
         self.layer = layer
         self.batch = batch
+        self._checked = set()
         self.capacity = layer.window if layer.main_ring else capacity
         alloc = torch.zeros if zero else torch.empty
         nm, ns = layer.n_main, layer.n_stream
@@ -494,13 +507,23 @@ def attn_decode_block(layer: Layer, cache: KVCache, q, k_new, v_new, past_lens, 
                                      epi, _stream(stream)))
 
 
+_plans = {}
+
+
 def head_plan(layer: Layer):
+    """duo_head_plan: (class per KV head, rank per KV head, n_main, n_stream);
+    memoised per layer description."""
+    key = _layer_key(layer)
+    hit = _plans.get(key)
+    if hit is not None:
+        return list(hit[0]), list(hit[1]), hit[2], hit[3]
     lib = load()
     n = layer.num_kv_heads
     cls, rank = (ctypes.c_int32 * n)(), (ctypes.c_int32 * n)()
     nm, ns = ctypes.c_int32(), ctypes.c_int32()
     cl = layer._c()
     _check(lib.duo_head_plan(ctypes.byref(cl), cls, rank, ctypes.byref(nm), ctypes.byref(ns)))
+    _plans[key] = (tuple(cls), tuple(rank), nm.value, ns.value)
     return list(cls), list(rank), nm.value, ns.value
 
 
