@@ -114,6 +114,7 @@ def load(path: str = LIB_PATH):
         "duo_attn_prefill": (ctypes.c_int, [LP, CP, i32, P, P, P, i32, i64, P, P, P, sz, PP, EP, P]),
         "duo_attn_prefill_workspace_bytes": (sz, [LP, i32, i32, i64]),
         "duo_attn_decode": (ctypes.c_int, [LP, CP, i32, P, P, i64, P, P, P, sz, PP, EP, P]),
+        "duo_attn_decode_noalloc": (ctypes.c_int, [LP, CP, i32, P, P, i64, P, P, PP, EP, P]),
         "duo_qk_prologue": (ctypes.c_int, [PP, i32, i32, i32, P, P, P, P]),
         "duo_rope_frequencies": (ctypes.c_int, [ctypes.POINTER(_Rope), ctypes.POINTER(ctypes.c_double)]),
         "duo_attn_decode_workspace_bytes": (sz, [LP, i32, i64]),
@@ -463,6 +464,27 @@ def attn_decode(layer: Layer, cache: KVCache, q, seq_lens, max_seq_len: int, out
     _check(lib.duo_attn_decode(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(q), _ptr(seq_lens),
                                int(max_seq_len), _ptr(out), _ptr(lse), _ptr(workspace), nbytes,
                                _prologue(q_prologue), epi, _stream(stream)))
+
+
+def attn_decode_noalloc(layer: Layer, cache: KVCache, q, seq_lens, max_seq_len: int, out, lse=None,
+                        stream=None, sink_logits=None, gate=None, q_prologue: Optional[Prologue] = None):
+    """duo_attn_decode_noalloc: attn_decode without a workspace (the library's
+    own scratch; calls on one GPU must not overlap)."""
+    B = q.shape[0]
+    hq = layer.num_q_heads
+    _need(q, "q", (B, hq, HEAD_DIM), "bfloat16")
+    _need(seq_lens, "seq_lens", (B,), "int32")
+    _need(out, "out", (B, hq, HEAD_DIM), "bfloat16")
+    _need(lse, "lse", (B, hq), "float32")
+    _need_prologue(q_prologue, "q_prologue")
+    _need_cache(cache, layer, B)
+    epi = _epilogue(out, sink_logits, gate)
+    _need_device(q=q, seq_lens=seq_lens, out=out, lse=lse)
+    lib = load()
+    cl, cc = layer._c(), cache._c()
+    _check(lib.duo_attn_decode_noalloc(ctypes.byref(cl), ctypes.byref(cc), B, _ptr(q), _ptr(seq_lens),
+                                       int(max_seq_len), _ptr(out), _ptr(lse), _prologue(q_prologue), epi,
+                                       _stream(stream)))
 
 
 def decode_block_workspace_bytes(layer: Layer, batch: int, num_tokens: int, max_past_len: int) -> int:

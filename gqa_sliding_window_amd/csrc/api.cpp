@@ -593,6 +593,53 @@ int duo_decode_plan(const duo_layer* layer, int32_t batch, int64_t max_seq_len, 
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation and parameters shared by duo_attn_decode and
+// duo_attn_decode_noalloc (everything but the workspace).
+int prepare_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch, const void* q,
+                   const int32_t* seq_lens, int64_t max_seq_len, void* out, float* lse,
+                   const duo_prologue* q_prologue, const duo_epilogue* epilogue, DecodeParams* p) {
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  if (max_seq_len <= 0 || max_seq_len > kMaxPos) return fail(DUO_ERR_INVALID_ARG, "max_seq_len out of range");
+  if (q == nullptr || seq_lens == nullptr || out == nullptr) return fail(DUO_ERR_INVALID_ARG, "q, seq_lens and out must not be NULL");
+  if (!aligned16(q) || !aligned16(out)) return fail(DUO_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
+  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(DUO_ERR_INVALID_ARG, "lse misaligned");
+  if ((rc = check_cache(L, cache, true, true))) return rc;
+  if (L.plan.n_main > 0 && !L.main_ring && max_seq_len > cache->main_capacity)
+    return fail(DUO_ERR_CAPACITY, "max_seq_len %lld exceeds main_capacity %lld", (long long)max_seq_len,
+                (long long)cache->main_capacity);
+  const int64_t main_cap = L.main_ring ? L.window : (L.plan.n_main > 0 ? cache->main_capacity : 1);
+  if ((rc = build_decode(L, batch, max_seq_len, main_cap, p))) return rc;
+  if ((rc = read_epilogue(epilogue, &p->sink_logits, &p->gate, &p->gate_mode))) return rc;
+  if ((rc = read_prologue(q_prologue, &p->qpro, &p->qpro_on))) return rc;
+  p->q = static_cast<const uint16_t*>(q);
+  p->seq_lens = seq_lens;
+  p->out = static_cast<uint16_t*>(out);
+  p->lse = lse;
+  p->k_main = static_cast<const uint16_t*>(cache->k_main);
+  p->v_main = static_cast<const uint16_t*>(cache->v_main);
+  p->k_stream = static_cast<const uint16_t*>(cache->k_stream);
+  p->v_stream = static_cast<const uint16_t*>(cache->v_stream);
+  return DUO_OK;
+}
+
+void attach_decode_ws(DecodeParams* p, void* workspace) {
+  const WsLayout wl = decode_ws_layout(*p);
+  char* ws = static_cast<char*>(workspace);
+  p->ws_count = reinterpret_cast<int32_t*>(ws + wl.count);
+  p->ws_ml = reinterpret_cast<float*>(ws + wl.ml);
+  p->ws_acc = reinterpret_cast<float*>(ws + wl.acc);
+}
+
+}  // namespace
+
+extern "C" {
+
 int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch, const void* q,
                     const int32_t* seq_lens, int64_t max_seq_len, void* out, float* lse, void* workspace,
                     size_t workspace_bytes, const duo_prologue* q_prologue, const duo_epilogue* epilogue,
@@ -602,37 +649,41 @@ int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t b
   if (rc) return rc;
   if (batch < 0) return fail(DUO_ERR_INVALID_ARG, "batch must be >= 0");
   if (batch == 0) return ok();
-  if (max_seq_len <= 0 || max_seq_len > kMaxPos) return fail(DUO_ERR_INVALID_ARG, "max_seq_len out of range");
-  if (q == nullptr || seq_lens == nullptr || out == nullptr) return fail(DUO_ERR_INVALID_ARG, "q, seq_lens and out must not be NULL");
-  if (!aligned16(q) || !aligned16(out)) return fail(DUO_ERR_INVALID_ARG, "q and out must be 16-byte aligned");
-  if (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u)) return fail(DUO_ERR_INVALID_ARG, "lse misaligned");
-  if ((rc = check_cache(L, cache, true, true))) return rc;
-  if (L.plan.n_main > 0 && !L.main_ring && max_seq_len > cache->main_capacity)
-    return fail(DUO_ERR_CAPACITY, "max_seq_len %lld exceeds main_capacity %lld", (long long)max_seq_len,
-                (long long)cache->main_capacity);
   DecodeParams p;
-  const int64_t main_cap = L.main_ring ? L.window : (L.plan.n_main > 0 ? cache->main_capacity : 1);
-  if ((rc = build_decode(L, batch, max_seq_len, main_cap, &p))) return rc;
+  rc = prepare_decode(layer, cache, batch, q, seq_lens, max_seq_len, out, lse, q_prologue, epilogue, &p);
+  if (rc) return rc;
   const size_t need = decode_ws_bytes(p);
   if (workspace == nullptr || workspace_bytes < need)
     return fail(DUO_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return fail(DUO_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  if ((rc = read_epilogue(epilogue, &p.sink_logits, &p.gate, &p.gate_mode))) return rc;
-  if ((rc = read_prologue(q_prologue, &p.qpro, &p.qpro_on))) return rc;
-  p.q = static_cast<const uint16_t*>(q);
-  p.seq_lens = seq_lens;
-  p.out = static_cast<uint16_t*>(out);
-  p.lse = lse;
-  p.k_main = static_cast<const uint16_t*>(cache->k_main);
-  p.v_main = static_cast<const uint16_t*>(cache->v_main);
-  p.k_stream = static_cast<const uint16_t*>(cache->k_stream);
-  p.v_stream = static_cast<const uint16_t*>(cache->v_stream);
-  const WsLayout wl = decode_ws_layout(p);
-  char* ws = static_cast<char*>(workspace);
-  p.ws_count = reinterpret_cast<int32_t*>(ws + wl.count);
-  p.ws_ml = reinterpret_cast<float*>(ws + wl.ml);
-  p.ws_acc = reinterpret_cast<float*>(ws + wl.acc);
+  attach_decode_ws(&p, workspace);
   return hip_status(launch_decode(p, static_cast<hipStream_t>(stream)), "decode launch");
+}
+
+int duo_attn_decode_noalloc(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch, const void* q,
+                            const int32_t* seq_lens, int64_t max_seq_len, void* out, float* lse,
+                            const duo_prologue* q_prologue, const duo_epilogue* epilogue, void* stream) {
+  Layer L;
+  int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  if (batch < 0) return fail(DUO_ERR_INVALID_ARG, "batch must be >= 0");
+  if (batch == 0) return ok();
+  DecodeParams p;
+  rc = prepare_decode(layer, cache, batch, q, seq_lens, max_seq_len, out, lse, q_prologue, epilogue, &p);
+  if (rc) return rc;
+  const size_t need = decode_ws_bytes(p);
+  if (need > noalloc_scratch_bytes())
+    return fail(DUO_ERR_WORKSPACE, "this decode needs %zu bytes of scratch; the library holds %zu (use duo_attn_decode)",
+                need, noalloc_scratch_bytes());
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  void* scratch = nullptr;
+  if ((rc = hip_status(noalloc_scratch(&scratch), "decode scratch"))) return rc;
+  attach_decode_ws(&p, scratch);
+  // the arrival counters start at zero on every call (a fill kernel, not a
+  // memset: safe under graph capture)
+  const int64_t counters = (int64_t)p.batch * p.hkv * p.n_cb;
+  if ((rc = hip_status(launch_fill_zero(p.ws_count, counters, s), "decode scratch clear"))) return rc;
+  return hip_status(launch_decode(p, s), "decode launch");
 }
 
 size_t duo_attn_decode_block_workspace_bytes(const duo_layer* layer, int32_t batch, int32_t num_tokens,

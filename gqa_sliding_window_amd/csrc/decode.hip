@@ -28,6 +28,8 @@
 #include "mfma_common.h"
 #include "qk_prologue.h"
 
+#include <mutex>
+
 namespace duo {
 
 constexpr int kDPitch = kD + 8;
@@ -626,6 +628,37 @@ hipError_t launch_decode_block(const DecodeParams& p, hipStream_t s) {
                          dim3((unsigned)(items8 * p.n_cb)), dim3(512), 0, s, p);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- no-allocation decode
+// Scratch held by the library for duo_attn_decode_noalloc (callers that cannot
+// allocate device memory): the same layout as a caller's decode workspace, in
+// one file-scope device array per GPU, kept until the process ends. In host
+// code `scratch` names a host-side stand-in, never the device memory: its
+// device address is resolved once per device with hipGetSymbolAddress, with
+// that device current, and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+hipError_t noalloc_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s) {

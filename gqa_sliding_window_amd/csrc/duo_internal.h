@@ -352,5 +352,9 @@ hipError_t launch_prefill(const PrefillParams& p, int64_t n_blocks, hipStream_t 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_block(const DecodeParams& p, hipStream_t s);
 hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s);
+// The library-held decode scratch of duo_attn_decode_noalloc: its size, and
+// its address on the current device (resolved once per device).
+size_t noalloc_scratch_bytes();
+hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace duo

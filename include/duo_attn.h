@@ -288,6 +288,23 @@ int duo_attn_decode(const duo_layer* layer, const duo_kv_cache* cache, int32_t b
                     void* out, float* lse, void* workspace, size_t workspace_bytes,
                     const duo_prologue* q_prologue, const duo_epilogue* epilogue, void* stream);
 
+/* duo_attn_decode without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). The split-K partials and arrival counters live in
+ * scratch the library holds: one 32 MiB device array per GPU, resolved on the
+ * first call on each device and kept until the process ends. Arguments and
+ * results are those of duo_attn_decode. A decode whose workspace
+ * (duo_attn_decode_workspace_bytes) would exceed 32 MiB is refused with
+ * DUO_ERR_WORKSPACE before anything is launched. Each call first clears the
+ * counters it uses (a fill kernel on `stream`, so it may be captured). The
+ * call allocates and frees nothing. Every call on one GPU shares that GPU's
+ * scratch: calls that may overlap on one GPU (different streams without
+ * ordering) race and give wrong results; order them on one stream. */
+int duo_attn_decode_noalloc(const duo_layer* layer, const duo_kv_cache* cache, int32_t batch,
+                            const void* q, const int32_t* seq_lens, int64_t max_seq_len, void* out,
+                            float* lse, const duo_prologue* q_prologue, const duo_epilogue* epilogue,
+                            void* stream);
+
 /* Block decode: num_tokens consecutive query tokens per sequence, at
  * positions past_lens[b] .. past_lens[b] + num_tokens - 1 -- the block a
  * speculative-decoding target verifies in one pass (SGLang cookbook

@@ -440,3 +440,25 @@ def test_binding_rejects_a_resized_cache_tensor(lib):
     kv = torch.zeros(1, 4, 8, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="k_stream"):
         g.kv_append(L, cache, kv, kv, torch.zeros(1, dtype=torch.int32), max_end_pos=4, stream=0)
+
+
+def test_noalloc_decode_refuses_sizes_beyond_its_scratch(lib):
+    """duo_attn_decode_noalloc keeps its partials in 32 MiB of library-held
+    scratch: a decode whose workspace would be larger is refused on the host,
+    with the sizes in the message, before any launch."""
+    L = Layer()
+    B, maxlen = 2048, 1024
+    need = g.decode_workspace_bytes(L, B, maxlen)
+    assert need > 32 << 20
+    q = FakeTensor((B, 48, 128))
+    sl = FakeTensor((B,))
+    rc = lib.load().duo_attn_decode_noalloc(ctypes.byref(L._c()), ctypes.byref(FakeCache(cap=maxlen)._c()), B,
+                                            q.data_ptr(), sl.data_ptr(), maxlen, q.data_ptr(), None, None, None,
+                                            None)
+    assert rc == -4
+    msg = lib.load().duo_last_error().decode()
+    assert str(need) in msg and str(32 << 20) in msg
+    # within the limit the host-side checks pass on to the usual argument errors
+    assert lib.load().duo_attn_decode_noalloc(ctypes.byref(L._c()), ctypes.byref(FakeCache(cap=1000)._c()), 4,
+                                              q.data_ptr(), None, 1000, q.data_ptr(), None, None, None,
+                                              None) == -1
