@@ -14,7 +14,7 @@ HBM):
   decode      -- KV GB/s of the sliding-window decode (batch 64, window-512
                  ring) and of the DuoAttention decode (batch 16, contexts up to
                  131072, Bernoulli(0.25) full-head mask), and of block decodes
-                 of 4 and 8 tokens after those contexts; algorithmic bytes =
+                 of 4, 6 and 8 tokens after those contexts; algorithmic bytes =
                  every visible K and V row read once per KV head; several cache
                  replicas are rotated so the 256 MB Infinity Cache cannot serve
                  them;
@@ -153,7 +153,8 @@ def bench_swa_prefill(torch, G, wl, timer, warmup, steps):
     layer = G.Layer(num_q_heads=w.hq, num_kv_heads=w.hkv, kind=G.SLIDING, window=w.window)
     flops = prefill_flops(G, layer, w.batch, w.seq)
     ms = timer.run(lambda i: G.attn_prefill(layer, q, k, v, out), warmup, steps)
-    wgs = len(G.prefill_plan(layer, w.batch, w.seq))
+    plan = G.prefill_plan(layer, w.batch, w.seq)
+    wgs = int((plan[:, 0] >= 0).sum())
     return {"workload": w.name, "algorithmic_flop": flops, "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
             "ms_median": timer.last["median_ms"], "ms_min": timer.last["min_ms"], "workgroups": wgs,
             "bound": f"latency: {wgs} workgroups for 256 CUs, one short wave of work; "
@@ -264,7 +265,7 @@ def bench_decode_duo(torch, G, wl, timer, warmup, steps, replicas=2):
     # block's own K/V
     block = {}
     gen.manual_seed(w.seed * 7919)
-    for T in (4, 8):
+    for T in (4, 6, 8):
         qb = torch.randn((w.batch, T, w.hq, 128), generator=gen, device="cuda").to(torch.bfloat16)
         kb = torch.randn((w.batch, T, w.hkv, 128), generator=gen, device="cuda").to(torch.bfloat16)
         vb = torch.randn((w.batch, T, w.hkv, 128), generator=gen, device="cuda").to(torch.bfloat16)

@@ -128,7 +128,7 @@ def load(path: str = LIB_PATH):
         "duo_decode_plan": (ctypes.c_int, [LP, i32, i64, I32P, I32P, I64P]),
         "duo_last_error": (ctypes.c_char_p, []),
         "duo_attn_version": (ctypes.c_int, []),
-        "duo_prefill_tile_rows": (ctypes.c_int, []),
+        "duo_prefill_tile_rows": (ctypes.c_int, [LP]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -549,20 +549,25 @@ def head_plan(layer: Layer):
     return list(cls), list(rank), nm.value, ns.value
 
 
-def prefill_tile_rows() -> int:
-    return int(load().duo_prefill_tile_rows())
+def prefill_tile_rows(layer: Layer) -> int:
+    """Query rows per prefill work item of this layer (64 or 128)."""
+    cl = layer._c()
+    rows = int(load().duo_prefill_tile_rows(ctypes.byref(cl)))
+    if rows < 0:
+        _check(rows)
+    return rows
 
 
 def prefill_plan(layer: Layer, batch: int, num_tokens: int, start_pos: int = 0, with_workspace: bool = False):
-    """Per workgroup (batch, q_head, q_tile, key_tiles, piece, pieces);
-    padding rows are (-1, -1, -1, 0, 0, 0)."""
+    """Per workgroup (batch, q_head, q_tile, key_tiles, piece, pieces, heads);
+    padding rows are (-1, -1, -1, 0, 0, 0, 0)."""
     import numpy as np
     lib = load()
     cl = layer._c()
     n = ctypes.c_int64()
     ws = 1 if with_workspace else 0
     _check(lib.duo_prefill_plan(ctypes.byref(cl), batch, num_tokens, start_pos, ws, None, ctypes.byref(n)))
-    items = np.zeros((n.value, 6), dtype=np.int32)
+    items = np.zeros((n.value, 7), dtype=np.int32)
     _check(lib.duo_prefill_plan(ctypes.byref(cl), batch, num_tokens, start_pos, ws,
                                 items.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), ctypes.byref(n)))
     return items

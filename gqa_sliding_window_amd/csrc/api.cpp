@@ -204,8 +204,8 @@ int choose_pieces(const PrefillParams& p) {
   int64_t wm = 0, ws = 0, lmax = 0;
   const int64_t last = p.start_pos + p.T - 1;
   for (int qt = 0; qt < p.n_qtiles; ++qt) {
-    const int64_t qa = p.start_pos + (int64_t)qt * kPrefillRows;
-    const int64_t qb = qa + kPrefillRows - 1 < last ? qa + kPrefillRows - 1 : last;
+    const int64_t qa = p.start_pos + (int64_t)qt * p.rows;
+    const int64_t qb = qa + p.rows - 1 < last ? qa + p.rows - 1 : last;
     KeyRange r0, r1;
     prefill_key_ranges(p, kMain, qa, qb, r0, r1);
     const int64_t nm = tiles_of(r0);
@@ -216,8 +216,9 @@ int choose_pieces(const PrefillParams& p) {
       ws += (nr > 0 ? tiles_of(r0) : 0) + (nr > 1 ? tiles_of(r1) : 0);
     }
   }
-  const int64_t per_qt_main = (int64_t)p.batch * p.n_main * p.group;  // workgroups per query tile
-  const int64_t total = (wm * p.n_main + ws * p.n_stream) * p.batch * p.group;
+  const int64_t gw = p.group / p.hpw;  // workgroups per unit
+  const int64_t per_qt_main = (int64_t)p.batch * p.n_main * gw;  // workgroups per query tile
+  const int64_t total = (wm * p.n_main + ws * p.n_stream) * p.batch * gw;
   const int64_t nm_wg = per_qt_main * p.n_qtiles;
   if (lmax * 2 * kPrefillSlots <= total) return 1;
   auto est = [&](int n) {
@@ -256,7 +257,9 @@ int build_prefill(const Layer& L, int32_t batch, int32_t T, int64_t start_pos, b
   p->n_main = L.plan.n_main;
   p->n_stream = L.plan.n_stream;
   p->stream_mask = L.plan.stream_mask;
-  p->n_qtiles = (T + kPrefillRows - 1) / kPrefillRows;
+  p->hpw = (L.group % 2 == 0) ? 2 : 1;
+  p->rows = kPrefillWaves * kPrefillWaveRows / p->hpw;
+  p->n_qtiles = (T + p->rows - 1) / p->rows;
   const int64_t um = (int64_t)p->n_qtiles * batch * L.plan.n_main;
   const int64_t us = (int64_t)p->n_qtiles * batch * L.plan.n_stream;
   if (um + us + kXcds > kMaxGrid / kMaxPieces) return fail(DUO_ERR_INVALID_ARG, "prefill work too large for one launch");
@@ -267,20 +270,20 @@ int build_prefill(const Layer& L, int32_t batch, int32_t T, int64_t start_pos, b
   p->scale_log2 = L.scale * 1.4426950408889634f;
   const int64_t virt = (int64_t)p->n_units_main8 * p->n_pieces + us;
   const int64_t units8 = (virt + kXcds - 1) / kXcds * kXcds;
-  *n_blocks = units8 * L.group;
+  *n_blocks = units8 * (L.group / p->hpw);
   if (*n_blocks > kMaxGrid) return fail(DUO_ERR_INVALID_ARG, "prefill grid too large");
   return DUO_OK;
 }
 
-// Prefill workspace: [n_units_main * group] int32 arrival counters |
-// [n_units_main * group * n_pieces] partial results of kPartFloats floats;
-// both parts 256-byte aligned. Empty without pieces.
+// Prefill workspace: one slot per (main unit, workgroup of the unit): [slots]
+// int32 arrival counters | [slots * n_pieces] partial results of kPartFloats
+// floats; both parts 256-byte aligned. Empty without pieces.
 struct PrefillWs { size_t part, total; };
 
 PrefillWs prefill_ws_layout(const PrefillParams& p) {
   PrefillWs w{0, 0};
   if (p.n_pieces <= 1) return w;
-  const size_t slots = (size_t)p.n_units_main * p.group;
+  const size_t slots = (size_t)p.n_units_main * (p.group / p.hpw);
   w.part = (slots * sizeof(int32_t) + 255) / 256 * 256;
   w.total = w.part + slots * p.n_pieces * (size_t)kPartFloats * sizeof(float);
   return w;
@@ -366,7 +369,13 @@ extern "C" {
 
 int duo_attn_version(void) { return DUO_ATTN_VERSION; }
 
-int duo_prefill_tile_rows(void) { return kPrefillRows; }
+int duo_prefill_tile_rows(const duo_layer* layer) {
+  Layer L;
+  const int rc = check_layer(layer, &L);
+  if (rc) return rc;
+  ok();
+  return kPrefillWaves * kPrefillWaveRows / (L.group % 2 == 0 ? 2 : 1);
+}
 
 const char* duo_last_error(void) { return g_err; }
 
@@ -481,19 +490,19 @@ int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens, 
   if (items) {
     for (int64_t i = 0; i < nb; ++i) {
       const PrefillItem it = prefill_item(p, (int)i);
-      int32_t* o = items + 6 * i;
+      int32_t* o = items + 7 * i;
       o[0] = o[1] = o[2] = -1;
-      o[3] = o[4] = 0;
-      o[5] = 0;
+      o[3] = o[4] = o[5] = o[6] = 0;
       if (!it.valid) continue;
-      const int64_t qa = start_pos + (int64_t)it.qtile * kPrefillRows;
+      const int64_t qa = start_pos + (int64_t)it.qtile * p.rows;
       const int64_t last = start_pos + num_tokens - 1;
-      const int64_t qb = qa + kPrefillRows - 1 < last ? qa + kPrefillRows - 1 : last;
+      const int64_t qb = qa + p.rows - 1 < last ? qa + p.rows - 1 : last;
       KeyRange r0, r1;
       const int nr = prefill_key_ranges(p, it.cls, qa, qb, r0, r1);
       const int64_t tiles = tiles_of(r0) + (nr > 1 ? tiles_of(r1) : 0);
       const PieceRange pr = piece_range((int)tiles, it.cls == kMain ? p.n_pieces : 1, it.piece);
       o[0] = it.b; o[1] = it.qhead; o[2] = it.qtile; o[3] = pr.t1 - pr.t0; o[4] = it.piece; o[5] = pr.used;
+      o[6] = p.hpw;
     }
   }
   return ok();

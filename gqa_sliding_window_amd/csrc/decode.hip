@@ -54,7 +54,11 @@ __device__ __forceinline__ void load_tile(const uint16_t* kbase, const uint16_t*
 // Block decode: key index k < n_valid is cache slot k, k >= n_valid is row
 // k - n_valid of the block's own K/V (stride `bstride` elements per token).
 // This wave loads rows ld_row + 4 j (j < kJ) of the tile starting at k0.
-template <int kJ>
+// kShared: another column block's workgroup streams the same keys at about
+// the same time on this XCD, so the loads keep their lines in the L2 for it
+// (ordinary loads; a single reader uses non-temporal ones). Verify blocks of
+// 36-48 columns: 224 -> 207 us on the Duo decode workload's contexts.
+template <int kJ, bool kShared>
 __device__ __forceinline__ void load_tile_block(const uint16_t* kbase, const uint16_t* vbase,
                                                 const uint16_t* kblk, const uint16_t* vblk, int64_t bstride,
                                                 int64_t n_valid, int64_t k0, int64_t k_end, int ld_row,
@@ -66,8 +70,10 @@ __device__ __forceinline__ void load_tile_block(const uint16_t* kbase, const uin
     const bool cached = key < n_valid;
     const uint16_t* kp = cached ? kbase + key * kD : kblk + (key - n_valid) * bstride;
     const uint16_t* vp = cached ? vbase + key * kD : vblk + (key - n_valid) * bstride;
-    stK[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + ld_chunk * 8));
-    stV[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + ld_chunk * 8));
+    const u32x4* ka = reinterpret_cast<const u32x4*>(kp + ld_chunk * 8);
+    const u32x4* va = reinterpret_cast<const u32x4*>(vp + ld_chunk * 8);
+    stK[j] = kShared ? *ka : __builtin_nontemporal_load(ka);
+    stV[j] = kShared ? *va : __builtin_nontemporal_load(va);
   }
 }
 
@@ -234,9 +240,10 @@ __device__ __forceinline__ void write_out_pair(const DecodeParams& p, int64_t bh
 // tiles in flight in registers: the same bytes in flight per CU as the
 // single-token kernel) into the slot's shared LDS tile, and each attends it
 // for its own 16 columns, so the cache is streamed once for 32 columns.
-template <bool kBlock, int kNH, bool kFused>
+template <bool kBlock, int kNH, bool kFused, bool kShared = false>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   static_assert(kNH == 1 || (kBlock && kNH == 2), "two halves only for the block decode");
+  static_assert(!kShared || kNH == 2, "shared key streams only between 32-column blocks");
   constexpr int kCols = 16 * kNH;
   constexpr int kNW = kDecodeWaves * kNH;      // waves per workgroup
   constexpr int kThreads = 64 * kNW;
@@ -391,7 +398,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     // order, so waiting for one buffer never waits for the other)
     auto load = [&](int64_t k0, u32x4 (&bk)[8], u32x4 (&bvv)[8]) {
       if (kBlock)
-        load_tile_block<8>(kbase, vbase, kblk, vblk, bstride, n_valid, k0, k_end, ld_row, ld_chunk, bk, bvv);
+        load_tile_block<8, false>(kbase, vbase, kblk, vblk, bstride, n_valid, k0, k_end, ld_row, ld_chunk, bk, bvv);
       else
         load_tile(kbase, vbase, k0, k_end, ld_row, ld_chunk, bk, bvv);
     };
@@ -428,7 +435,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     const int64_t nt = (k_end - k_begin + stride - 1) / stride;
     u32x4 xK[4][4], xV[4][4];  // four half tiles in flight
     auto load = [&](int64_t k0, u32x4 (&bk)[4], u32x4 (&bvv)[4]) {
-      load_tile_block<4>(kbase, vbase, kblk, vblk, bstride, n_valid, k0, k_end, ld_row, ld_chunk, bk, bvv);
+      load_tile_block<4, kShared>(kbase, vbase, kblk, vblk, bstride, n_valid, k0, k_end, ld_row, ld_chunk, bk, bvv);
     };
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -600,9 +607,15 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) { decode_body<false, 1, false>(p); }
 __global__ __launch_bounds__(256, 2) void decode_block16_kernel(DecodeParams p) { decode_body<true, 1, false>(p); }
 __global__ __launch_bounds__(512, 1) void decode_block_kernel(DecodeParams p) { decode_body<true, 2, false>(p); }
+__global__ __launch_bounds__(512, 1) void decode_block_shared_kernel(DecodeParams p) {
+  decode_body<true, 2, false, true>(p);
+}
 __global__ __launch_bounds__(256, 2) void decode_fused_kernel(DecodeParams p) { decode_body<false, 1, true>(p); }
 __global__ __launch_bounds__(256, 2) void decode_block16_fused_kernel(DecodeParams p) { decode_body<true, 1, true>(p); }
 __global__ __launch_bounds__(512, 1) void decode_block_fused_kernel(DecodeParams p) { decode_body<true, 2, true>(p); }
+__global__ __launch_bounds__(512, 1) void decode_block_shared_fused_kernel(DecodeParams p) {
+  decode_body<true, 2, true, true>(p);
+}
 
 static bool fused(const DecodeParams& p) { return p.qpro_on || p.sink_logits != nullptr || p.gate != nullptr; }
 
@@ -620,12 +633,15 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t s) {
 hipError_t launch_decode_block(const DecodeParams& p, hipStream_t s) {
   const int64_t items8 = ((int64_t)p.n_items + kXcds - 1) / kXcds * kXcds;
   if (p.n_items > 0) {
+    const dim3 grid((unsigned)(items8 * p.n_cb));
+    const bool f = fused(p);
     if (p.T * p.group <= 16)  // one 16-column block: the 4-wave form
-      hipLaunchKernelGGL(fused(p) ? decode_block16_fused_kernel : decode_block16_kernel,
-                         dim3((unsigned)(items8 * p.n_cb)), dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL(fused(p) ? decode_block_fused_kernel : decode_block_kernel,
-                         dim3((unsigned)(items8 * p.n_cb)), dim3(512), 0, s, p);
+      hipLaunchKernelGGL(f ? decode_block16_fused_kernel : decode_block16_kernel, grid, dim3(256), 0, s, p);
+    else if (p.n_cb == 1)
+      hipLaunchKernelGGL(f ? decode_block_fused_kernel : decode_block_kernel, grid, dim3(512), 0, s, p);
+    else  // several 32-column blocks stream the same keys
+      hipLaunchKernelGGL(f ? decode_block_shared_fused_kernel : decode_block_shared_kernel, grid, dim3(512), 0, s,
+                         p);
   }
   return hipGetLastError();
 }

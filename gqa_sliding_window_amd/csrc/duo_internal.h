@@ -12,10 +12,10 @@ namespace duo {
 constexpr int kD = 128;           // head_dim
 constexpr int kMaxKv = 32;        // KV heads per layer
 constexpr int kMaxGroup = 16;     // query heads per KV head (MFMA columns)
-#ifndef DUO_PREFILL_ROWS
-#define DUO_PREFILL_ROWS 128
-#endif
-constexpr int kPrefillRows = DUO_PREFILL_ROWS;  // query rows per prefill workgroup
+// A prefill workgroup is 4 waves of 32 query rows: 64 rows of two query
+// heads of one KV head (even group sizes), else 128 rows of one query head.
+constexpr int kPrefillWaveRows = 32;
+constexpr int kPrefillWaves = 4;
 constexpr int kPrefillKeys = 64;  // keys per prefill K/V tile
 // Prefill key-range split: resident prefill workgroups on an MI355X (256 CUs,
 // two 4-wave workgroups per CU), the most pieces one unit's keys are cut into,
@@ -146,13 +146,15 @@ struct PrefillParams {
   int32_t sink, recent;
   int32_t n_main, n_stream;
   uint32_t stream_mask;
+  int32_t rows;          // query rows per unit: 64 (two query heads per workgroup) or 128 (one)
+  int32_t hpw;           // query heads per workgroup: 2 or 1
   int32_t n_qtiles;
   int32_t n_units_main;  // (q tile, batch, main head) units
   int32_t n_units;       // all units
   int32_t n_units_main8; // n_units_main rounded up to a multiple of kXcds
   int32_t n_pieces;      // key-range pieces per main unit (1: no split)
-  int32_t* ws_count;     // [n_units_main, group] arrival counters, zero between calls
-  float* ws_part;        // [n_units_main, group, n_pieces] partial results (kPartFloats each)
+  int32_t* ws_count;     // [n_units_main, group / hpw] arrival counters, zero between calls
+  float* ws_part;        // [n_units_main, group / hpw, n_pieces] partial results (kPartFloats each)
   float scale_log2;      // scale * log2(e)
   const float* sink_logits;  // [Hq] attention-sink logits (natural units) or null
   const uint16_t* gate;      // bf16 output gate or null
@@ -169,14 +171,15 @@ struct PrefillItem {
   int32_t piece;  // key-range piece of a main unit (0 for streaming units)
 };
 
-// Workgroup -> work item. Units (one kPrefillRows-row query tile of one
-// KV-head group) are ordered main-class units before streaming units. A main
+// Workgroup -> work item. Units (one `rows`-row query tile of one KV-head
+// group) are ordered main-class units before streaming units. A workgroup
+// computes `hpw` consecutive query heads of its unit (qhead is the first). A main
 // unit may be cut into n_pieces key-range pieces (long units of a chunked
 // prefill over a long past), each a workgroup of its own; its pieces are merged
 // by the last one to finish. Unit u runs on XCD u % 8 (workgroups are
-// dispatched to XCDs round-robin); the `group` query heads of one unit, and
-// its pieces, are consecutive on that XCD, so they share the unit's K/V tiles
-// through its L2. When a class's (batch, KV head) groups fill whole 8-wide
+// dispatched to XCDs round-robin); the workgroups of the `group` query heads
+// of one unit, and its pieces, are consecutive on that XCD, so they share the
+// unit's K/V tiles through its L2. When a class's (batch, KV head) groups fill whole 8-wide
 // stripes, each XCD takes its groups one at a time, later query tiles first;
 // otherwise all groups advance together, later query tiles first, so every
 // XCD gets an equal share of each cost level. The main class is padded to a
@@ -187,8 +190,9 @@ __host__ __device__ inline PrefillItem prefill_item(const PrefillParams& p, int 
   PrefillItem it{};
   const int x = block % kXcds;
   const int s = block / kXcds;
-  const int vu = (s / p.group) * kXcds + x;  // virtual unit
-  const int g = s % p.group;
+  const int gw = p.group / p.hpw;           // workgroups per unit and piece
+  const int vu = (s / gw) * kXcds + x;      // virtual unit
+  const int g = (s % gw) * p.hpw;
   const int main_v = p.n_units_main8 * p.n_pieces;
   int u, n_class;
   if (vu < main_v) {

@@ -394,17 +394,20 @@ int duo_head_plan(const duo_layer* layer, int32_t* head_class, int32_t* head_ran
 
 /* Prefill work plan (host only): the number of workgroups the prefill launch
  * uses, with a workspace (with_workspace != 0) or without one; when `items`
- * is not NULL it receives, per workgroup, six int32 (batch, q_head, q_tile,
- * key_tiles, piece, pieces), or (-1, -1, -1, 0, 0, 0) for padding, with q_tile
- * a duo_prefill_tile_rows()-row tile of the chunk, key_tiles the 64-key tiles
- * the workgroup visits after masked tiles are skipped, and piece / pieces its
+ * is not NULL it receives, per workgroup, seven int32 (batch, q_head, q_tile,
+ * key_tiles, piece, pieces, heads), or (-1, -1, -1, 0, 0, 0, 0) for padding:
+ * the workgroup computes query heads q_head .. q_head + heads - 1 on the
+ * q_tile-th duo_prefill_tile_rows()-row tile of the chunk, visiting key_tiles
+ * 64-key tiles after masked tiles are skipped; piece / pieces are its
  * key-range piece and the number of non-empty pieces of its query tile (1
  * when the tile runs whole; a workgroup with key_tiles 0 is an empty piece). */
 int duo_prefill_plan(const duo_layer* layer, int32_t batch, int32_t num_tokens,
                      int64_t start_pos, int32_t with_workspace, int32_t* items, int64_t* n_items);
 
-/* Query rows per prefill work item (the q_tile unit of duo_prefill_plan). */
-int duo_prefill_tile_rows(void);
+/* Query rows per prefill work item of this layer (the q_tile unit of
+ * duo_prefill_plan): 64 when a workgroup computes two query heads (even
+ * group sizes), else 128. A negative duo_status on an invalid layer. */
+int duo_prefill_tile_rows(const duo_layer* layer);
 
 /* Decode work plan (host only): keys per split and number of split-K work
  * items; when `items` is not NULL it receives per item four int32

@@ -19,7 +19,8 @@ int main(void) {
   L.window = 0; L.sink = 64; L.recent = 256; L.full_attention_heads = mask; L.scale = 0.f;
 
   CHECK(duo_attn_version() == DUO_ATTN_VERSION);
-  CHECK(duo_prefill_tile_rows() > 0);
+  CHECK(duo_prefill_tile_rows(&L) == 64);  /* group 6: two heads per workgroup */
+  CHECK(duo_prefill_tile_rows(NULL) == DUO_ERR_INVALID_ARG);
 
   /* head plan: full heads 1 and 4 ranked 0, 1; the rest streaming, ranked in order */
   int32_t cls[8], rank[8], nm = -1, ns = -1;
@@ -59,12 +60,12 @@ int main(void) {
   r.theta = 1.f;
   CHECK(duo_rope_frequencies(&r, f) == DUO_ERR_INVALID_ARG);
 
-  /* work plans: count, then fill (6 int32 per prefill item, 4 per decode item) */
+  /* work plans: count, then fill (7 int32 per prefill item, 4 per decode item) */
   {
     int64_t n = 0;
     CHECK(duo_prefill_plan(&L, 2, 300, 0, 0, NULL, &n) == DUO_OK);
     CHECK(n > 0 && n < 100000);
-    int32_t* items = (int32_t*)malloc((size_t)n * 6 * sizeof(int32_t));
+    int32_t* items = (int32_t*)malloc((size_t)n * 7 * sizeof(int32_t));
     CHECK(items != NULL);
     CHECK(duo_prefill_plan(&L, 2, 300, 0, 0, items, &n) == DUO_OK);
     free(items);
@@ -72,7 +73,7 @@ int main(void) {
     CHECK(duo_attn_prefill_workspace_bytes(&L, 1, 8192, 8192 * 15) > 0);
     CHECK(duo_attn_prefill_workspace_bytes(&L, 4, 8192, 0) == 0);
     CHECK(duo_prefill_plan(&L, 1, 8192, 8192 * 15, 1, NULL, &n) == DUO_OK);
-    items = (int32_t*)malloc((size_t)n * 6 * sizeof(int32_t));
+    items = (int32_t*)malloc((size_t)n * 7 * sizeof(int32_t));
     CHECK(items != NULL);
     CHECK(duo_prefill_plan(&L, 1, 8192, 8192 * 15, 1, items, &n) == DUO_OK);
     CHECK(items[5] > 1);

@@ -169,14 +169,18 @@ def test_prefill_plan_covers_every_tile_once_and_skips_masked(lib, case):
     L, B, T, P = case["layer"], case["B"], case["T"], case["P"]
     items = g.prefill_plan(L, B, T, P)
     real = items[items[:, 0] >= 0]
-    rows = g.prefill_tile_rows()
-    nqt = (T + rows - 1) // rows
-    assert len(real) == B * L.num_q_heads * nqt
-    assert len({tuple(r[:3]) for r in real}) == len(real)
-    assert (real[:, 4] == 0).all() and (real[:, 5] == 1).all()  # no pieces without a workspace
+    rows = g.prefill_tile_rows(L)
     G = L.num_q_heads // L.num_kv_heads
+    hpw = 2 if G % 2 == 0 else 1
+    assert rows == 128 // hpw and (real[:, 6] == hpw).all()
+    nqt = (T + rows - 1) // rows
+    assert len(real) * hpw == B * L.num_q_heads * nqt
+    heads = [(b, h + j, qt) for b, h, qt in real[:, :3] for j in range(hpw)]
+    assert len(set(heads)) == len(heads) == B * L.num_q_heads * nqt
+    assert all(h // G == (h + hpw - 1) // G for h in real[:, 1])  # one KV head per workgroup
+    assert (real[:, 4] == 0).all() and (real[:, 5] == 1).all()  # no pieces without a workspace
     mask = L.full_attention_heads
-    for b, h, qt, nt, _, _ in real:
+    for b, h, qt, nt, _, _, _ in real:
         qa = P + rows * qt
         qb = min(qa + rows - 1, P + T - 1)
         streaming = mask is not None and mask[h // G] == 0
@@ -218,12 +222,13 @@ def test_prefill_plan_pieces_cover_each_query_tile_once(lib, case):
     L, B, T, P = case["layer"], case["B"], case["T"], case["P"]
     items = g.prefill_plan(L, B, T, P, with_workspace=True)
     real = items[items[:, 0] >= 0]
-    rows = g.prefill_tile_rows()
+    rows = g.prefill_tile_rows(L)
     G = L.num_q_heads // L.num_kv_heads
     mask = L.full_attention_heads
     by_tile = {}
-    for b, h, qt, nt, piece, pieces in real:
-        by_tile.setdefault((b, h, qt), []).append((piece, pieces, nt))
+    for b, h, qt, nt, piece, pieces, hpw in real:
+        for j in range(hpw):
+            by_tile.setdefault((b, h + j, qt), []).append((piece, pieces, nt))
     nqt = (T + rows - 1) // rows
     assert len(by_tile) == B * L.num_q_heads * nqt
     cut = 0
@@ -243,8 +248,8 @@ def test_prefill_plan_pieces_cover_each_query_tile_once(lib, case):
     nbytes = g.prefill_workspace_bytes(L, B, T, P)
     if cut:
         n_pieces = max(p[0] for ps in by_tile.values() for p in ps) + 1
-        n_main_tiles = B * L.n_main * nqt * G
-        assert nbytes >= n_main_tiles * n_pieces * (4 * 2 * 8 * 64 * 4 + 4 * 2 * 16 * 2) * 4
+        n_main_wgs = B * L.n_main * nqt * G // int(real[0, 6])
+        assert nbytes >= n_main_wgs * n_pieces * (4 * 2 * 8 * 64 * 4 + 4 * 2 * 16 * 2) * 4
     else:
         assert nbytes == 0
     if P == 8192 * 15:
