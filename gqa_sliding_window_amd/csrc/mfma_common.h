@@ -62,6 +62,24 @@ __device__ __forceinline__ float wave_xor_max(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask));
 }
 
+// Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 on the VALU (no LDS
+// instruction): each row swap leaves lane l's value and its partner's, in the
+// other 16-lane (then 32-lane) half, in the two results.
+__device__ __forceinline__ float lane4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Sum over lanes l, l ^ 16, l ^ 32 and l ^ 48, the same way.
+__device__ __forceinline__ float lane4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kLog2e = 1.4426950408889634f;

@@ -64,6 +64,7 @@ struct KvSrc {
   int cls;
   int ring_cap;          // main ring capacity (0 = contiguous main cache)
   int sink, recent;
+  int chunk_end;          // P + T: first position past the chunk
 };
 
 // Cache slot of a past position (library slot contract, see duo_attn.h).
@@ -86,40 +87,47 @@ __device__ __forceinline__ Src row_src(const KvSrc& s, int pos) {
   return r;
 }
 
-// Addressing of one tile's rows: from one base pointer and a row stride when
-// the whole tile lies in the chunk or in a stretch of the cache where
-// slot = position, else row by row (positions outside the range clamped onto
-// it: their logits are masked, their values are finite data).
+// Addressing of one tile's rows. A tile that starts in the chunk, or lies
+// wholly in a stretch of the cache where slot = position, is loaded from one
+// base pointer and a row stride, whatever part of it the key range covers:
+// its rows outside the range are valid keys and values whose logits are
+// masked, and rows past the chunk's end lie outside the load's buffer and
+// read as zeros. Other tiles are loaded row by row (positions outside the
+// range clamped onto it: their logits are masked, their values are finite
+// data).
 struct TileAddr {
   const uint16_t* k;
   const uint16_t* v;
   uint32_t stride_b;  // bytes between consecutive rows (fast form)
+  uint32_t bytes;     // bytes of the tile's rows that exist, from k / v (fast form)
   bool general;       // row-by-row form
 };
 
-__device__ __forceinline__ TileAddr tile_addr(const KvSrc& s, const TileRange& r, int lo) {
+__device__ __forceinline__ TileAddr tile_addr(const KvSrc& s, int lo) {
   const int hi = lo + kPrefillKeys - 1;
-  const bool inside = lo >= r.lo && hi <= r.hi;
   TileAddr a;
   a.general = false;
-  if (inside && lo >= s.P) {
+  if (lo >= s.P) {
     const int64_t off = (int64_t)(lo - s.P) * s.cstride;
     a.k = s.ck + off;
     a.v = s.cv + off;
     a.stride_b = (uint32_t)s.cstride * 2u;
+    a.bytes = (uint32_t)min(s.chunk_end - 1 - lo, kPrefillKeys - 1) * a.stride_b + kD * 2u;
     return a;
   }
   const bool contiguous_cache = hi < s.P && (s.cls == kStream ? hi < s.sink : s.ring_cap == 0);
-  if (inside && contiguous_cache) {
+  if (contiguous_cache) {
     const int64_t off = (int64_t)lo * kD;
     a.k = s.mk + off;
     a.v = s.mv + off;
     a.stride_b = kD * 2u;
+    a.bytes = kPrefillKeys * kD * 2u;
     return a;
   }
   a.k = s.mk;
   a.v = s.mv;
   a.stride_b = 0;
+  a.bytes = 0;
   a.general = true;
   return a;
 }
@@ -162,13 +170,19 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const KvSrc& s, const Ti
                                          const TileAddr& ta, int wave, const SlotMap<kV>& map) {
   uint16_t* dst = lds + wave * 512;
   if (!ta.general) {
-    // uniform base + 32-bit lane offset (row < 64, stride < 2^24 bytes)
-    const char* base = reinterpret_cast<const char*>(kV ? ta.v : ta.k);
+    // buffer loads from a raw buffer over the tile's rows (descriptor word
+    // 3: 32-bit data format) + a 32-bit lane offset (row < 64, stride < 2^24
+    // bytes). A global load into LDS is a flat access to both memories, and
+    // while one is in flight the compiler makes every LDS read wait for all
+    // outstanding LDS operations; with buffer loads in flight the K and V
+    // fragment reads keep their partial waits.
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kV ? ta.v : ta.k), 0, (int)ta.bytes, 0x00020000);
 #pragma unroll
     for (int jj = 0; jj < SlotMap<kV>::kPerWave; ++jj) {
       if (SlotMap<kV>::active(wave, jj)) {
         const uint32_t off = __umul24(map.row[jj], ta.stride_b) + map.colb[jj];
-        __builtin_amdgcn_global_load_lds((const void*)(base + off), (lds_void*)(dst + jj * 512 * kWaves), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + jj * 512 * kWaves), 16, off, 0, 0, 0);
       }
     }
     return;
@@ -183,6 +197,9 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const KvSrc& s, const Ti
       __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + jj * 512 * kWaves), 16, 0, 0);
     }
   }
+  // the row-by-row form (tiles across start_pos or in a cache ring) waits
+  // for its global loads here, so that none is in flight at the LDS reads
+  __builtin_amdgcn_s_waitcnt(0);
 }
 
 // kHeads query heads of one KV head per workgroup: waves w and w + 2 of a
@@ -270,6 +287,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
   src.ring_cap = p.main_ring ? (int)p.main_cap : 0;
   src.sink = p.sink;
   src.recent = p.recent;
+  src.chunk_end = P + p.T;
   if (it.cls == kStream) {
     const int64_t off = ((int64_t)it.b * p.n_stream + it.rank) * (int64_t)(p.sink + p.recent) * kD;
     src.mk = p.k_stream + off;
@@ -304,7 +322,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
   auto issue = [&](int idx, uint16_t* dk, uint16_t* dv) {
     const TileRange& r = idx < nt0 ? rg0 : rg1;
     const int lo = tile_lo(idx);
-    const TileAddr ta = tile_addr(src, r, lo);
+    const TileAddr ta = tile_addr(src, lo);
     dma_tile<false>(dk, src, r, lo, ta, wave, kmap);
     dma_tile<true>(dv, src, r, lo, ta, wave, vmap);
   };
@@ -339,15 +357,24 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
       for (int t = 0; t < kRT; ++t)
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) s[t][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // K fragments one 32-column step ahead of their MFMAs (the fences
+      // keep the compiler from regrouping the reads behind full waits)
+      bf16x8 kb[2][4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) kb[0][kt] = kfirst[kt];
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) {
+        if (ds < 3) {
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          const bf16x8 a =
-              ds == 0 ? kfirst[kt] : *reinterpret_cast<const bf16x8*>(&cK[(16 * kt + r16) * kPitch + 32 * ds + 8 * g]);
-#pragma unroll
-          for (int t = 0; t < kRT; ++t) s[t][kt] = mfma_16x16x32(a, qf[t][ds], s[t][kt]);
+          for (int kt = 0; kt < 4; ++kt)
+            kb[(ds + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(&cK[(16 * kt + r16) * kPitch + 32 * (ds + 1) + 8 * g]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+          for (int t = 0; t < kRT; ++t) s[t][kt] = mfma_16x16x32(kb[ds & 1][kt], qf[t][ds], s[t][kt]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     if (idx + 1 < t_end) issue(idx + 1, nK, nV);
@@ -371,6 +398,18 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
             }
         }
       }
+      // the first V fragments are read before the softmax, whose
+      // arithmetic covers their latency; the rest stay 4 steps ahead
+      const uint16_t* vbase = &cV[(4 * g + (r16 >> 2)) * kVPitch + 4 * (r16 & 3)];
+      i16x4 vr[4][2];
+      auto vread = [&](int n, i16x4* d) {
+        const uint16_t* v0 = vbase + 32 * (n >> 3) * kVPitch + 16 * (n & 7);
+        d[0] = lds_read_tr16(v0);
+        d[1] = lds_read_tr16(v0 + 16 * kVPitch);
+      };
+#pragma unroll
+      for (int n = 0; n < 4; ++n) vread(n, vr[n]);
+      __builtin_amdgcn_sched_barrier(0);
       // Online softmax. Each lane holds 16 logits of each of its rows; the
       // 4 lanes of a row share the row maximum. The maximum only moves when
       // some lane's logits exceed it by the rescale threshold, so the
@@ -379,18 +418,19 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
       bool grow = false;
 #pragma unroll
       for (int t = 0; t < kRT; ++t) {
-        float v = fmaxf(fmaxf(s[t][0][0], s[t][0][1]), fmaxf(s[t][0][2], s[t][0][3]));
+        // chained three-way maxima: 8 instructions for 16 values
+        float v = fmaxf(fmaxf(s[t][0][0], s[t][0][1]), s[t][0][2]);
 #pragma unroll
-        for (int kt = 1; kt < 4; ++kt)
-          v = fmaxf(fmaxf(v, fmaxf(s[t][kt][0], s[t][kt][1])), fmaxf(s[t][kt][2], s[t][kt][3]));
+        for (int j = 3; j < 15; j += 2)
+          v = fmaxf(fmaxf(v, s[t][j >> 2][j & 3]), s[t][(j + 1) >> 2][(j + 1) & 3]);
+        v = fmaxf(v, s[t][3][3]);
         lmx[t] = v * c;
         grow = grow || lmx[t] > m[t] + kRescaleThreshold;
       }
       if (__any(grow)) {
 #pragma unroll
         for (int t = 0; t < kRT; ++t) {
-          float mx = wave_xor_max(lmx[t], 16);
-          mx = wave_xor_max(mx, 32);
+          const float mx = lane4_max(lmx[t]);
           const bool up = mx > m[t] + kRescaleThreshold;
           const float a = up ? fast_exp2(m[t] - mx) : 1.f;
           m[t] = up ? mx : m[t];
@@ -417,15 +457,18 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
         pb[t][1] = pack_bf16(s[t][2], s[t][3]);
       }
       // O^T += V^T P^T
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
-        const uint16_t* v0 = &cV[(32 * kk + 4 * g + (r16 >> 2)) * kVPitch + 4 * (r16 & 3)];
-        const uint16_t* v1 = v0 + 16 * kVPitch;
 #pragma unroll
         for (int dt = 0; dt < 8; ++dt) {
-          const bf16x8 a = cat_bf16(lds_read_tr16(v0 + 16 * dt), lds_read_tr16(v1 + 16 * dt));
+          const int n = kk * 8 + dt;
+          const bf16x8 a = cat_bf16(vr[n & 3][0], vr[n & 3][1]);
+          if (n + 4 < 16) vread(n + 4, vr[n & 3]);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int t = 0; t < kRT; ++t) o[t][dt] = mfma_16x16x32(a, pb[t][kk], o[t][dt]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
@@ -444,9 +487,28 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
 
   // row sums: the 4 lanes of a row each hold the sum over their own keys
 #pragma unroll
-  for (int t = 0; t < kRT; ++t) {
-    l[t] += __shfl_xor(l[t], 16);
-    l[t] += __shfl_xor(l[t], 32);
+  for (int t = 0; t < kRT; ++t) l[t] = lane4_sum(l[t]);
+
+  // The rest reads its parameters afresh from the kernel arguments (at an
+  // index the compiler cannot see is 0): keeping them in scalar registers
+  // across the tile loop spilled scalars there and cost the loop its
+  // overlapped LDS reads.
+  int zero = 0;
+  __asm__ volatile("" : "+s"(zero));
+  const PrefillParams& pf = (&p)[zero];
+  const PrefillItem itf = prefill_item(pf, blockIdx.x);
+  const int qheadf = itf.qhead + wave / kRowWaves;
+  const int Pf = (int)pf.start_pos;
+  const int qaf = Pf + itf.qtile * kRows;
+  const int qbf = min(qaf + kRows - 1, Pf + pf.T - 1);
+  const int qw0f = qaf + rwave * 16 * kRT;
+  const bool wave_activef = qw0f <= qbf;
+  PieceRange prf;
+  {
+    KeyRange k0, k1;
+    const int nr = prefill_key_ranges(pf, itf.cls, qaf, qbf, k0, k1);
+    const int nt = (int)tiles_of(k0) + (nr > 1 ? (int)tiles_of(k1) : 0);
+    prf = piece_range(nt, itf.cls == kMain ? pf.n_pieces : 1, itf.piece);
   }
 
   // ---- key-range pieces: every piece publishes its partial (running max,
@@ -456,11 +518,11 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
   // own included, and combines them in piece order (max, rescale, add), so
   // the result does not depend on which piece finished last; it finishes the
   // rows below and resets the counter for the next call.
-  if (pr.used > 1) {
-    const int gw = p.group / kHeads;  // workgroups per unit and piece
-    const int64_t cslot = (int64_t)it.unit * gw + (it.qhead - it.kvh * p.group) / kHeads;
-    const float* parts = p.ws_part + cslot * p.n_pieces * kPartFloats;
-    float* mine = p.ws_part + (cslot * p.n_pieces + it.piece) * kPartFloats;
+  if (prf.used > 1) {
+    const int gw = pf.group / kHeads;  // workgroups per unit and piece
+    const int64_t cslot = (int64_t)itf.unit * gw + (itf.qhead - itf.kvh * pf.group) / kHeads;
+    const float* parts = pf.ws_part + cslot * pf.n_pieces * kPartFloats;
+    float* mine = pf.ws_part + (cslot * pf.n_pieces + itf.piece) * kPartFloats;
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
 #pragma unroll
@@ -473,12 +535,12 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
     }
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    int32_t* counter = p.ws_count + cslot;
+    int32_t* counter = pf.ws_count + cslot;
     if (tid == 0)
-      s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == pr.used - 1);
+      s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == prf.used - 1);
     __syncthreads();
     if (!s_last) return;
-    for (int q = 0; q < pr.used; ++q) {
+    for (int q = 0; q < prf.used; ++q) {
       const float* src = parts + (int64_t)q * kPartFloats;
 #pragma unroll
       for (int t = 0; t < kRT; ++t) {
@@ -501,39 +563,39 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
     if (tid == 0) __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  if (!wave_active) return;
+  if (!wave_activef) return;
   // ---- epilogue: O = O^T / l (with the attention sink, if any, in l), times
   // the output gate, bf16 round-to-nearest-even; lse = (m + log2 l) ln 2
 #pragma unroll
   for (int t = 0; t < kRT; ++t) {
     const float lt = l[t];
-    const int qpos = qw0 + 16 * t + r16;
-    if (qpos > qb) continue;
+    const int qpos = qw0f + 16 * t + r16;
+    if (qpos > qbf) continue;
     float inv = 1.f / lt;
     const float mu = (m[t] == kNegInf) ? 0.f : m[t];
     float lse = (mu + __log2f(lt)) * kLn2;
-    if (kFused && p.sink_logits != nullptr) {
-      const RowNorm rn = row_norm(m[t], lt, p.sink_logits, qhead);
+    if (kFused && pf.sink_logits != nullptr) {
+      const RowNorm rn = row_norm(m[t], lt, pf.sink_logits, qheadf);
       inv = rn.inv;
       lse = rn.lse;
     }
-    const int64_t orow = ((int64_t)it.b * p.T + (qpos - P)) * p.hq + qhead;
-    uint16_t* dst = p.out + orow * kD + 4 * g;
-    if (!kFused || p.gate == nullptr) {
+    const int64_t orow = ((int64_t)itf.b * pf.T + (qpos - Pf)) * pf.hq + qheadf;
+    uint16_t* dst = pf.out + orow * kD + 4 * g;
+    if (!kFused || pf.gate == nullptr) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const bf16x4 v = pack_bf16x4(o[t][dt] * inv);
         *reinterpret_cast<bf16x4*>(dst + 16 * dt) = v;
       }
-    } else if (p.gate_mode == 2) {
-      const float f = inv * gate_factor(bf16_bits_to_f32(p.gate[orow]));
+    } else if (pf.gate_mode == 2) {
+      const float f = inv * gate_factor(bf16_bits_to_f32(pf.gate[orow]));
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const bf16x4 v = pack_bf16x4(o[t][dt] * f);
         *reinterpret_cast<bf16x4*>(dst + 16 * dt) = v;
       }
     } else {
-      const uint16_t* gsrc = p.gate + orow * kD + 4 * g;
+      const uint16_t* gsrc = pf.gate + orow * kD + 4 * g;
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
         const uint2 gw = *reinterpret_cast<const uint2*>(gsrc + 16 * dt);
@@ -543,7 +605,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
         *reinterpret_cast<bf16x4*>(dst + 16 * dt) = v;
       }
     }
-    if (p.lse != nullptr && g == 0) p.lse[((int64_t)it.b * p.hq + qhead) * p.T + (qpos - P)] = lse;
+    if (pf.lse != nullptr && g == 0) pf.lse[((int64_t)itf.b * pf.hq + qheadf) * pf.T + (qpos - Pf)] = lse;
   }
 }
 
