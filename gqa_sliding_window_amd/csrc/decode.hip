@@ -29,6 +29,7 @@
 #include "qk_prologue.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace duo {
 
@@ -407,7 +408,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     __builtin_amdgcn_sched_barrier(0);
     load(first + stride, bK, bV);
     __builtin_amdgcn_sched_barrier(0);
-    for (int64_t t = 0; t < nt; t += 2) {
+    int64_t t = 0;
+    for (; t + 2 < nt; t += 2) {
       const int64_t k0 = first + t * stride;
       stage_tile(sK, sV, ld_row, ld_chunk, aK, aV);
       __builtin_amdgcn_sched_barrier(0);
@@ -418,6 +420,22 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       stage_tile(sK, sV, ld_row, ld_chunk, bK, bV);
       __builtin_amdgcn_sched_barrier(0);
       load(k0 + 3 * stride, bK, bV);
+      __builtin_amdgcn_sched_barrier(0);
+      attend_tile<kBlock>(sK, sV, qf, k0 + stride, k_end, c, r16, g, m, l, o, bv, mask_all);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // The last pass (the wave's last one or two tiles) issues no loads: a
+    // batch-64 sliding-window decode streams 4 tiles per wave, and the two
+    // extra tile loads of the clamped last key per wave cost 4% there
+    // (27.3 -> 26.2 us). Peeled rather than predicated: a predicated load
+    // makes the compiler wait for every outstanding load before staging.
+    if (t < nt) {
+      const int64_t k0 = first + t * stride;
+      stage_tile(sK, sV, ld_row, ld_chunk, aK, aV);
+      __builtin_amdgcn_sched_barrier(0);
+      attend_tile<kBlock>(sK, sV, qf, k0, k_end, c, r16, g, m, l, o, bv, mask_all);
+      __builtin_amdgcn_sched_barrier(0);
+      stage_tile(sK, sV, ld_row, ld_chunk, bK, bV);
       __builtin_amdgcn_sched_barrier(0);
       attend_tile<kBlock>(sK, sV, qf, k0 + stride, k_end, c, r16, g, m, l, o, bv, mask_all);
       __builtin_amdgcn_sched_barrier(0);
@@ -442,26 +460,34 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       load(first + i * stride, xK[i], xV[i]);
       __builtin_amdgcn_sched_barrier(0);
     }
-    auto step = [&](int64_t t, u32x4 (&bk)[4], u32x4 (&bvv)[4], uint16_t* sK, uint16_t* sV) {
+    auto step = [&](int64_t t, auto with_load, u32x4 (&bk)[4], u32x4 (&bvv)[4], uint16_t* sK, uint16_t* sV) {
       const int64_t k0 = first + t * stride;
       stage_rows(sK, sV, ld_row, ld_chunk, bk, bvv);
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
-      load(k0 + 4 * stride, bk, bvv);
+      if constexpr (decltype(with_load)::value) load(k0 + 4 * stride, bk, bvv);
       __builtin_amdgcn_sched_barrier(0);
       if (half < n_half)  // a half without columns only helps load and stage
         attend_tile<kBlock>(sK, sV, qf, k0, k_end, c, r16, g, m, l, o, bv, mask_all);
       __builtin_amdgcn_sched_barrier(0);
     };
-    for (int64_t t = 0; t < nt; t += 4) {
-      step(t, xK[0], xV[0], sK0, sV0);
-      if (t + 1 >= nt) break;
-      step(t + 1, xK[1], xV[1], sK1, sV1);
-      if (t + 2 >= nt) break;
-      step(t + 2, xK[2], xV[2], sK0, sV0);
-      if (t + 3 >= nt) break;
-      step(t + 3, xK[3], xV[3], sK1, sV1);
+    // Whole passes of four steps, then at most three steps that load
+    // nothing. (A pass that could break out after any step left the loop
+    // head with an inexact wait: its first staging waited for all four half
+    // tiles in flight, draining the stream every fourth tile; verify blocks
+    // of 6-8 tokens 204 -> 194 us on the Duo decode workload's contexts.)
+    const std::true_type loads{};
+    const std::false_type no_loads{};
+    int64_t t = 0;
+    for (; t + 4 <= nt; t += 4) {
+      step(t, loads, xK[0], xV[0], sK0, sV0);
+      step(t + 1, loads, xK[1], xV[1], sK1, sV1);
+      step(t + 2, loads, xK[2], xV[2], sK0, sV0);
+      step(t + 3, loads, xK[3], xV[3], sK1, sV1);
     }
+    if (t < nt) step(t, no_loads, xK[0], xV[0], sK0, sV0);
+    if (t + 1 < nt) step(t + 1, no_loads, xK[1], xV[1], sK1, sV1);
+    if (t + 2 < nt) step(t + 2, no_loads, xK[2], xV[2], sK0, sV0);
   }
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
