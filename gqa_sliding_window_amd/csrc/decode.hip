@@ -236,21 +236,29 @@ __device__ __forceinline__ void write_out_pair(const DecodeParams& p, int64_t bh
 // kNH = 1 (the single-token decode, and a block of at most 16 columns): 4
 // waves, each streaming its own 32-key tiles through a private LDS tile, two
 // tiles in flight in registers.
-// kNH = 2 (a block of more columns): 8 waves in 4 key slots x 2 column halves
-// of 16. The two waves of a slot load half of each 32-key tile each (4 half
-// tiles in flight in registers: the same bytes in flight per CU as the
+// kNH = 2 (a block of 17-32 columns): 8 waves in 4 key slots x 2 column
+// halves of 16. The two waves of a slot load half of each 32-key tile each (4
+// half tiles in flight in registers: the same bytes in flight per CU as the
 // single-token kernel) into the slot's shared LDS tile, and each attends it
 // for its own 16 columns, so the cache is streamed once for 32 columns.
+// kNH = 3 (blocks of 48 columns): the same 8 waves; half 0 attends column
+// blocks 0 and 2, half 1 block 1, and the loads are split 6 : 10 row groups
+// per tile so that both fit their registers with 3 tiles in flight. The
+// cache is streamed once for 48 columns (verify blocks of 6-8 tokens at
+// G = 6: T = 6 198 -> 175 us, T = 8 193 -> 182 us against two 32-column
+// blocks on the Duo decode workload's contexts).
 template <bool kBlock, int kNH, bool kFused, bool kShared = false>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
-  static_assert(kNH == 1 || (kBlock && kNH == 2), "two halves only for the block decode");
-  static_assert(!kShared || kNH == 2, "shared key streams only between 32-column blocks");
+  static_assert(kNH == 1 || (kBlock && (kNH == 2 || kNH == 3)), "two or three column blocks only for the block decode");
+  static_assert(!kShared || kNH >= 2, "shared key streams only between 32- or 48-column blocks");
   constexpr int kCols = 16 * kNH;
-  constexpr int kNW = kDecodeWaves * kNH;      // waves per workgroup
+  constexpr int kHalves = kNH == 1 ? 1 : 2;
+  constexpr int kNW = kDecodeWaves * kHalves;  // waves per workgroup
   constexpr int kThreads = 64 * kNW;
   // K/V tiles (single token: one per wave; block: two per key slot, used
   // alternately); reused after the key loop for the combine/merge.
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kDecodeWaves * 2 * kNH * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kDecodeWaves * 2 * kHalves * kTileElems];
+  static_assert(kDecodeWaves * kCols * kD * 4 <= (int)sizeof(smem), "combine area fits the tile area");
   __shared__ float s_ml[kDecodeWaves][kCols][2];
   __shared__ int s_last;
 
@@ -268,7 +276,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int slot = wave % kDecodeWaves;  // key slot: tiles k_begin + 32 (slot + 4 t)
-  const int half = wave / kDecodeWaves;  // column half of the block decode
+  const int half = wave / kDecodeWaves;  // column half (48 columns: half 0 takes blocks 0 and 2)
   const int lane = tid & 63;
   const int r16 = lane & 15;
   const int g = lane >> 4;
@@ -338,7 +346,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     // token t at past + t.
     if (kFused && p.qpro_on) prologue_frag(qf, kBlock ? (int)len + (col0 + hc) / G : (int)len - 1, g, p.qpro);
   }
-
+  // 48-column blocks: half 0 also attends column block 2 (lane column hc2)
+  const int hc2 = 32 + r16;
   // Block decode: visibility of each key for this lane's query token.
   BlockVis bv{};
   bool mask_all = false;
@@ -372,6 +381,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       bv.rem = rel - bv.wraps * ring_len;
     }
     mask_all = ring_len > 0;  // a band: the oldest cached positions can fall out of it
+
     kblk = p.k_new + ((int64_t)it.b * T * p.hkv + it.kvh) * kD;
     vblk = p.v_new + ((int64_t)it.b * T * p.hkv + it.kvh) * kD;
   }
@@ -440,7 +450,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       attend_tile<kBlock>(sK, sV, qf, k0 + stride, k_end, c, r16, g, m, l, o, bv, mask_all);
       __builtin_amdgcn_sched_barrier(0);
     }
-  } else {
+  } else if constexpr (kNH == 2) {
     // The slot's two LDS tiles, used alternately: one workgroup barrier per
     // tile orders this tile's staging before its reads, and every read of
     // the other tile (two tiles back) before its next staging.
@@ -488,6 +498,124 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     if (t < nt) step(t, no_loads, xK[0], xV[0], sK0, sV0);
     if (t + 1 < nt) step(t + 1, no_loads, xK[1], xV[1], sK1, sV1);
     if (t + 2 < nt) step(t + 2, no_loads, xK[2], xV[2], sK0, sV0);
+  } else {
+    // 48 columns, the cache streamed once: a 32-key tile is 16 groups of 4
+    // rows (8 of K, 8 of V); the waves of half 0, which attend two column
+    // blocks, load 6 groups of each tile, those of half 1 the other 10, so
+    // that both fit their registers with four tiles in flight (the same
+    // bytes in flight per CU as the 32-column form).
+    uint16_t* sK0 = smem + slot * 4 * kTileElems;
+    uint16_t* sV0 = sK0 + kTileElems;
+    uint16_t* sK1 = sV0 + kTileElems;
+    uint16_t* sV1 = sK1 + kTileElems;
+    const int64_t nt = (k_end - k_begin + stride - 1) / stride;
+    // state of column block 2 (half 0 only)
+    struct Second {
+      bf16x8 qf[4];
+      BlockVis bv;
+      float m, l;
+      f32x4 o[8];
+    };
+    auto stream = [&](auto n_groups, auto group0, auto two_blocks, Second& sec) {
+      constexpr int kG = decltype(n_groups)::value;
+      constexpr int kG0 = decltype(group0)::value;
+      constexpr bool kTwo = decltype(two_blocks)::value;
+      constexpr int kDepth = 3;  // tiles in flight
+      u32x4 x[kDepth][kG];
+      auto load = [&](int64_t k0, u32x4 (&bx)[kG]) {
+#pragma unroll
+        for (int i = 0; i < kG; ++i) {
+          const int gi = kG0 + i;
+          int64_t key = k0 + 4 * (gi & 7) + (lane >> 4);
+          key = key < k_end ? key : k_end - 1;
+          const bool cached = key < n_valid;
+          const uint16_t* src = gi < 8 ? (cached ? kbase + key * kD : kblk + (key - n_valid) * bstride)
+                                       : (cached ? vbase + key * kD : vblk + (key - n_valid) * bstride);
+          const u32x4* a = reinterpret_cast<const u32x4*>(src + ld_chunk * 8);
+          bx[i] = kShared ? *a : __builtin_nontemporal_load(a);
+        }
+      };
+#pragma unroll
+      for (int i = 0; i < kDepth; ++i) {
+        load(first + i * stride, x[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      auto step = [&](int64_t t, auto with_load, u32x4 (&bx)[kG], uint16_t* sK, uint16_t* sV) {
+        const int64_t k0 = first + t * stride;
+#pragma unroll
+        for (int i = 0; i < kG; ++i) {
+          const int gi = kG0 + i;
+          const int off = (4 * (gi & 7) + (lane >> 4)) * kDPitch + ld_chunk * 8;
+          *reinterpret_cast<u32x4*>(&(gi < 8 ? sK : sV)[off]) = bx[i];
+        }
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (decltype(with_load)::value) load(k0 + kDepth * stride, bx);
+        __builtin_amdgcn_sched_barrier(0);
+        if (half < n_half) attend_tile<kBlock>(sK, sV, qf, k0, k_end, c, r16, g, m, l, o, bv, mask_all);
+        if constexpr (kTwo)
+          if (n_half > 2) attend_tile<kBlock>(sK, sV, sec.qf, k0, k_end, c, r16, g, sec.m, sec.l, sec.o, sec.bv, mask_all);
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      const std::true_type loads{};
+      const std::false_type no_loads{};
+      // passes of six steps (register buffer t mod 3, LDS tile t mod 2);
+      // then at most five steps, of which only the first three load (their
+      // tiles may lie past the end: clamped reads, fully masked)
+      int64_t t = 0;
+      for (; t + 6 <= nt; t += 6) {
+        step(t, loads, x[0], sK0, sV0);
+        step(t + 1, loads, x[1], sK1, sV1);
+        step(t + 2, loads, x[2], sK0, sV0);
+        step(t + 3, loads, x[0], sK1, sV1);
+        step(t + 4, loads, x[1], sK0, sV0);
+        step(t + 5, loads, x[2], sK1, sV1);
+      }
+      if (t < nt) step(t, loads, x[0], sK0, sV0);
+      if (t + 1 < nt) step(t + 1, loads, x[1], sK1, sV1);
+      if (t + 2 < nt) step(t + 2, loads, x[2], sK0, sV0);
+      if (t + 3 < nt) step(t + 3, no_loads, x[0], sK1, sV1);
+      if (t + 4 < nt) step(t + 4, no_loads, x[1], sK0, sV0);
+    };
+    if (half == 0) {
+      Second sec;
+      {
+        const bool ok = hc2 < n_cols;
+        const uint16_t* src = p.q + row_of(ok ? hc2 : 0) * kD + 8 * g;
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) {
+          u32x4 raw = ok ? *reinterpret_cast<const u32x4*>(src + 32 * ds) : u32x4{0u, 0u, 0u, 0u};
+          sec.qf[ds] = __builtin_bit_cast(bf16x8, raw);
+        }
+        if (kFused && p.qpro_on) prologue_frag(sec.qf, (int)len + (col0 + hc2) / G, g, p.qpro);
+        // the same bands, for the query token of lane column hc2
+        sec.bv = bv;
+        sec.bv.q_pos = bv.past + (ok ? col0 + hc2 : col0) / G;
+        if (bv.lo != INT32_MIN) sec.bv.lo = bv.lo + (sec.bv.q_pos - bv.q_pos);
+        sec.m = kNegInf;
+        sec.l = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) sec.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      stream(std::integral_constant<int, 6>{}, std::integral_constant<int, 0>{}, std::true_type{}, sec);
+      sec.l += __shfl_xor(sec.l, 16);
+      sec.l += __shfl_xor(sec.l, 32);
+      // every wave is past its last tile: block 2's partial into the
+      // combine area (over the tiles)
+      __syncthreads();
+      float* comb = reinterpret_cast<float*>(smem);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+        *reinterpret_cast<f32x4*>(&comb[(slot * kCols + hc2) * kD + 16 * dt + 4 * g]) = sec.o[dt];
+      if (g == 0) {
+        s_ml[slot][hc2][0] = sec.m;
+        s_ml[slot][hc2][1] = sec.l;
+      }
+    } else {
+      Second none;
+      stream(std::integral_constant<int, 10>{}, std::integral_constant<int, 6>{}, std::false_type{}, none);
+      __syncthreads();
+    }
   }
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
@@ -502,6 +630,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     s_ml[slot][hc][0] = m;
     s_ml[slot][hc][1] = l;
   }
+
   __syncthreads();
 
   // thread -> (column, dim pair) of the item's columns; 64 threads per column
@@ -633,12 +762,20 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) { decode_body<false, 1, false>(p); }
 __global__ __launch_bounds__(256, 2) void decode_block16_kernel(DecodeParams p) { decode_body<true, 1, false>(p); }
 __global__ __launch_bounds__(512, 1) void decode_block_kernel(DecodeParams p) { decode_body<true, 2, false>(p); }
+__global__ __launch_bounds__(512, 1) void decode_block48_kernel(DecodeParams p) { decode_body<true, 3, false>(p); }
+__global__ __launch_bounds__(512, 1) void decode_block48_shared_kernel(DecodeParams p) {
+  decode_body<true, 3, false, true>(p);
+}
 __global__ __launch_bounds__(512, 1) void decode_block_shared_kernel(DecodeParams p) {
   decode_body<true, 2, false, true>(p);
 }
 __global__ __launch_bounds__(256, 2) void decode_fused_kernel(DecodeParams p) { decode_body<false, 1, true>(p); }
 __global__ __launch_bounds__(256, 2) void decode_block16_fused_kernel(DecodeParams p) { decode_body<true, 1, true>(p); }
 __global__ __launch_bounds__(512, 1) void decode_block_fused_kernel(DecodeParams p) { decode_body<true, 2, true>(p); }
+__global__ __launch_bounds__(512, 1) void decode_block48_fused_kernel(DecodeParams p) { decode_body<true, 3, true>(p); }
+__global__ __launch_bounds__(512, 1) void decode_block48_shared_fused_kernel(DecodeParams p) {
+  decode_body<true, 3, true, true>(p);
+}
 __global__ __launch_bounds__(512, 1) void decode_block_shared_fused_kernel(DecodeParams p) {
   decode_body<true, 2, true, true>(p);
 }
@@ -661,13 +798,16 @@ hipError_t launch_decode_block(const DecodeParams& p, hipStream_t s) {
   if (p.n_items > 0) {
     const dim3 grid((unsigned)(items8 * p.n_cb));
     const bool f = fused(p);
-    if (p.T * p.group <= 16)  // one 16-column block: the 4-wave form
+    const int cols = p.T * p.group;
+    if (cols <= 16)  // one 16-column block: the 4-wave form
       hipLaunchKernelGGL(f ? decode_block16_fused_kernel : decode_block16_kernel, grid, dim3(256), 0, s, p);
-    else if (p.n_cb == 1)
+    else if (cols <= 32)  // one 32-column block
       hipLaunchKernelGGL(f ? decode_block_fused_kernel : decode_block_kernel, grid, dim3(512), 0, s, p);
-    else  // several 32-column blocks stream the same keys
-      hipLaunchKernelGGL(f ? decode_block_shared_fused_kernel : decode_block_shared_kernel, grid, dim3(512), 0, s,
-                         p);
+    else if (p.n_cb == 1)  // one 48-column block
+      hipLaunchKernelGGL(f ? decode_block48_fused_kernel : decode_block48_kernel, grid, dim3(512), 0, s, p);
+    else  // several 48-column blocks stream the same keys
+      hipLaunchKernelGGL(f ? decode_block48_shared_fused_kernel : decode_block48_shared_kernel, grid, dim3(512), 0,
+                         s, p);
   }
   return hipGetLastError();
 }

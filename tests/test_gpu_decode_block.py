@@ -69,7 +69,7 @@ def check_block(layer, past, T, q, k, v, out, lse, what):
 
 CASES = {
     "full_T4_multisplit": (dict(), [1, 700, 2999, 64], 4),
-    "full_T8_two_column_blocks": (dict(), [0, 130, 1500], 8),
+    "full_T8_one_48_column_block": (dict(), [0, 130, 1500], 8),
     "full_T1": (dict(), [5, 1000], 1),
     "sliding_T4_wrapped": (dict(kind=1, window=512), [100, 511, 512, 513, 2000], 4),
     "sliding_T8_window_64": (dict(kind=1, window=64), [0, 63, 64, 70, 300], 8),
@@ -79,8 +79,8 @@ CASES = {
     "all_streaming_T2": (dict(full_attention_heads=[0] * 8), [64, 319, 320, 1000], 2),
     "group16_T3": (dict(num_q_heads=32, num_kv_heads=2), [77, 1200], 3),
     "duo_T7_partial_second_block": (dict(full_attention_heads=[0, 1, 0, 0, 0, 0, 0, 1]), [0, 5, 700, 3000], 7),
-    "duo_T10_two_blocks_ragged": (dict(full_attention_heads=[1, 0, 0, 0, 0, 1, 0, 0]), [0, 64, 900, 4000], 10),
-    "full_T16_three_blocks": (dict(), [3, 333, 2048], 16),
+    "duo_T10_two_48_column_blocks_ragged": (dict(full_attention_heads=[1, 0, 0, 0, 0, 1, 0, 0]), [0, 64, 900, 4000], 10),
+    "full_T16_two_full_48_column_blocks": (dict(), [3, 333, 2048], 16),
     "group16_T64_largest_block": (dict(num_q_heads=32, num_kv_heads=2, kind=1, window=512), [0, 100, 2000], 64),
     "duo_sliding_layer_T5": (dict(kind=1, window=100, full_attention_heads=[1, 0], sink=5, recent=7,
                                   num_q_heads=4, num_kv_heads=2), [0, 6, 12, 99, 100, 101, 450], 5),
@@ -141,8 +141,8 @@ def test_block_workspace_reuse_and_smaller_call(lib):
 @pytest.mark.parametrize("T", [4, 8])
 def test_block_decode_duo_workload(lib, T):
     """The verify-block launches the bench times: T = 4 (24 columns, one
-    32-column block) and T = 8 (48 columns, two blocks that share the key
-    stream) tokens after the Duo decode workload's contexts (batch 16, 48/8
+    32-column block) and T = 8 (48 columns, one 48-column block) tokens
+    after the Duo decode workload's contexts (batch 16, 48/8
     heads, contexts U[32768, 131072], its Bernoulli(0.25) mask), every row
     against the oracle."""
     import torch

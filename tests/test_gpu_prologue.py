@@ -182,15 +182,17 @@ def test_prefill_with_prologue(lib, name):
     assert np.abs(o_raw - o_ref[:2000]).max() > 0.1
 
 
-def test_decode_and_block_decode_with_prologue(lib):
+@pytest.mark.parametrize("T", [4, 7])
+def test_decode_and_block_decode_with_prologue(lib, T):
     """Caches filled through kv_append's k prologue; the decode's fused q
     prologue at position L - 1, the block decode's at past + t (its own K
-    through the standalone prologue first)."""
+    through the standalone prologue first). T = 4: one 32-column block; T = 7:
+    one 48-column block whose third column block is partly filled."""
     import torch
-    announce("decode + block decode with prologue")
+    announce(f"decode + block decode with prologue T={T}")
     layer = lib.Layer(full_attention_heads=[0, 1, 0, 0, 1, 0, 0, 0])
     hq, hkv = layer.num_q_heads, layer.num_kv_heads
-    lengths, T = [1, 300, 4500, 20000], 4
+    lengths = [1, 300, 4500, 20000]
     B = len(lengths)
     wq, wk = _weight(31), _weight(32)
     ends = [L + T for L in lengths]
