@@ -314,8 +314,9 @@ int build_decode(const Layer& L, int32_t batch, int64_t max_seq_len, int64_t mai
   p->window = L.main_ring ? L.window : 0;
   p->T = block_tokens > 0 ? block_tokens : 1;
   // column blocks per work item: 16 columns (one MFMA width) for the
-  // single-token decode, 32 (two halves sharing each K/V tile) for a block
-  // column blocks: one of at most 32 (T G) columns, else blocks of 48
+  // single-token decode; for a block, one block of at most 32 (T G) columns,
+  // else blocks of 48 (each workgroup streams the item's keys once for its
+  // columns)
   p->n_cb = block_tokens > 0 ? (p->T * L.group <= 32 ? 1 : (p->T * L.group + 47) / 48) : (L.group + 15) / 16;
   const int64_t extra = block_tokens;  // the block's own keys follow the cached ones
   const int64_t keys_main = (L.main_ring ? (max_seq_len < L.window ? max_seq_len : L.window) : max_seq_len) + extra;

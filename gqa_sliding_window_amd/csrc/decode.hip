@@ -19,7 +19,8 @@
 // running (max, sum, output); the waves are combined through LDS.
 // The block decode (T query tokens per sequence, attend then append) uses
 // the same body with (token, head) columns: up to 16 columns in this 4-wave
-// form, more in 32-column blocks of 8 waves (see decode_body).
+// form, more in 32- or 48-column blocks of 2 key slots x 2 column halves
+// (see decode_body).
 // A sequence whose keys fit one split is finished by its workgroup. Otherwise
 // each split stores its combined partial in the workspace and bumps the
 // group's arrival counter; the last workgroup to arrive merges all partials
@@ -236,30 +237,38 @@ __device__ __forceinline__ void write_out_pair(const DecodeParams& p, int64_t bh
 // kNH = 1 (the single-token decode, and a block of at most 16 columns): 4
 // waves, each streaming its own 32-key tiles through a private LDS tile, two
 // tiles in flight in registers.
-// kNH = 2 (a block of 17-32 columns): 8 waves in 4 key slots x 2 column
+// kNH = 2 (a block of 17-32 columns): 4 waves in 2 key slots x 2 column
 // halves of 16. The two waves of a slot load half of each 32-key tile each (4
-// half tiles in flight in registers: the same bytes in flight per CU as the
-// single-token kernel) into the slot's shared LDS tile, and each attends it
-// for its own 16 columns, so the cache is streamed once for 32 columns.
-// kNH = 3 (blocks of 48 columns): the same 8 waves; half 0 attends column
+// half tiles in flight in registers) into the slot's shared LDS tile, and
+// each attends it for its own 16 columns, so the cache is streamed once for
+// 32 columns.
+// kNH = 3 (blocks of 48 columns): the same 4 waves; half 0 attends column
 // blocks 0 and 2, half 1 block 1, and the loads are split 6 : 10 row groups
 // per tile so that both fit their registers with 3 tiles in flight. The
 // cache is streamed once for 48 columns (verify blocks of 6-8 tokens at
 // G = 6: T = 6 198 -> 175 us, T = 8 193 -> 182 us against two 32-column
 // blocks on the Duo decode workload's contexts).
+// Two workgroups of 4 waves share a CU in every form, so the split plan's
+// items fill 512 resident slots (one 8-wave workgroup of 4 key slots per CU
+// left this workload's 514 non-empty items a second, partly filled round:
+// T = 4 / 6 / 8 147 / 172 / 179 -> 145 / 156 / 165 us).
 template <bool kBlock, int kNH, bool kFused, bool kShared = false>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   static_assert(kNH == 1 || (kBlock && (kNH == 2 || kNH == 3)), "two or three column blocks only for the block decode");
   static_assert(!kShared || kNH >= 2, "shared key streams only between 32- or 48-column blocks");
   constexpr int kCols = 16 * kNH;
   constexpr int kHalves = kNH == 1 ? 1 : 2;
-  constexpr int kNW = kDecodeWaves * kHalves;  // waves per workgroup
+  // key slots per workgroup: 4 in the single-token form, 2 (x 2 halves) in
+  // a block form
+  constexpr int kSlots = kNH == 1 ? kDecodeWaves : 2;
+  constexpr int kNW = kSlots * kHalves;  // waves per workgroup
   constexpr int kThreads = 64 * kNW;
   // K/V tiles (single token: one per wave; block: two per key slot, used
   // alternately); reused after the key loop for the combine/merge.
-  __shared__ __attribute__((aligned(16))) uint16_t smem[kDecodeWaves * 2 * kHalves * kTileElems];
-  static_assert(kDecodeWaves * kCols * kD * 4 <= (int)sizeof(smem), "combine area fits the tile area");
-  __shared__ float s_ml[kDecodeWaves][kCols][2];
+  __shared__ __attribute__((aligned(16))) uint16_t smem[kSlots * 2 * kHalves * kTileElems];
+  static_assert(kSlots * kCols * kD * 4 <= (int)sizeof(smem), "combine area fits the tile area");
+  static_assert(2 * 16 * kDecodeMaxSplits * 4 + 16 * 4 <= (int)sizeof(smem), "merge area fits the tile area");
+  __shared__ float s_ml[kSlots][kCols][2];
   __shared__ int s_last;
 
   // Block decode: workgroup i runs on XCD i % 8 (round-robin dispatch); the
@@ -275,8 +284,8 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   const DecodeItem it = decode_item(p, item);
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
-  const int slot = wave % kDecodeWaves;  // key slot: tiles k_begin + 32 (slot + 4 t)
-  const int half = wave / kDecodeWaves;  // column half (48 columns: half 0 takes blocks 0 and 2)
+  const int slot = wave % kSlots;  // key slot: tiles k_begin + 32 (slot + kSlots t)
+  const int half = wave / kSlots;  // column half (48 columns: half 0 takes blocks 0 and 2)
   const int lane = tid & 63;
   const int r16 = lane & 15;
   const int g = lane >> 4;
@@ -392,11 +401,11 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Tiles of key slot `slot` start at k_begin + 32 * (slot + 4 t). Loads are
+  // Tiles of key slot `slot` start at k_begin + 32 * (slot + kSlots t). Loads are
   // issued unconditionally so the wait counts stay exact: a tile past the
   // split end reads the last valid key and is fully masked, leaving (m, l, o)
   // unchanged.
-  const int64_t stride = (int64_t)kDecodeKeys * kDecodeWaves;
+  const int64_t stride = (int64_t)kDecodeKeys * kSlots;
   const int64_t first = k_begin + (int64_t)kDecodeKeys * slot;
   const int ld_chunk = lane & 15;
   if (kNH == 1) {
@@ -620,7 +629,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
 
-  // ---- combine the 4 key slots: acc[slot][col][dim] in LDS (reuses the tile area)
+  // ---- combine the key slots: acc[slot][col][dim] in LDS (reuses the tile area)
   __syncthreads();
   float* comb = reinterpret_cast<float*>(smem);  // [4][kCols][128] floats
 #pragma unroll
@@ -640,10 +649,10 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     const int dim = 2 * (e % (kD / 2));
     float M = kNegInf;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, s_ml[w][col][0]);
+    for (int w = 0; w < kSlots; ++w) M = fmaxf(M, s_ml[w][col][0]);
     float L = 0.f, a0 = 0.f, a1 = 0.f;
 #pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
+    for (int w = 0; w < kSlots; ++w) {
       const float mw = s_ml[w][col][0];
       const float sc = (mw == kNegInf) ? 0.f : fast_exp2(mw - M);
       L += sc * s_ml[w][col][1];
@@ -761,22 +770,22 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
 // a q prologue, sink logits or a gate.
 __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeParams p) { decode_body<false, 1, false>(p); }
 __global__ __launch_bounds__(256, 2) void decode_block16_kernel(DecodeParams p) { decode_body<true, 1, false>(p); }
-__global__ __launch_bounds__(512, 1) void decode_block_kernel(DecodeParams p) { decode_body<true, 2, false>(p); }
-__global__ __launch_bounds__(512, 1) void decode_block48_kernel(DecodeParams p) { decode_body<true, 3, false>(p); }
-__global__ __launch_bounds__(512, 1) void decode_block48_shared_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_block_kernel(DecodeParams p) { decode_body<true, 2, false>(p); }
+__global__ __launch_bounds__(256, 2) void decode_block48_kernel(DecodeParams p) { decode_body<true, 3, false>(p); }
+__global__ __launch_bounds__(256, 2) void decode_block48_shared_kernel(DecodeParams p) {
   decode_body<true, 3, false, true>(p);
 }
-__global__ __launch_bounds__(512, 1) void decode_block_shared_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_block_shared_kernel(DecodeParams p) {
   decode_body<true, 2, false, true>(p);
 }
 __global__ __launch_bounds__(256, 2) void decode_fused_kernel(DecodeParams p) { decode_body<false, 1, true>(p); }
 __global__ __launch_bounds__(256, 2) void decode_block16_fused_kernel(DecodeParams p) { decode_body<true, 1, true>(p); }
-__global__ __launch_bounds__(512, 1) void decode_block_fused_kernel(DecodeParams p) { decode_body<true, 2, true>(p); }
-__global__ __launch_bounds__(512, 1) void decode_block48_fused_kernel(DecodeParams p) { decode_body<true, 3, true>(p); }
-__global__ __launch_bounds__(512, 1) void decode_block48_shared_fused_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_block_fused_kernel(DecodeParams p) { decode_body<true, 2, true>(p); }
+__global__ __launch_bounds__(256, 2) void decode_block48_fused_kernel(DecodeParams p) { decode_body<true, 3, true>(p); }
+__global__ __launch_bounds__(256, 2) void decode_block48_shared_fused_kernel(DecodeParams p) {
   decode_body<true, 3, true, true>(p);
 }
-__global__ __launch_bounds__(512, 1) void decode_block_shared_fused_kernel(DecodeParams p) {
+__global__ __launch_bounds__(256, 2) void decode_block_shared_fused_kernel(DecodeParams p) {
   decode_body<true, 2, true, true>(p);
 }
 
@@ -802,11 +811,11 @@ hipError_t launch_decode_block(const DecodeParams& p, hipStream_t s) {
     if (cols <= 16)  // one 16-column block: the 4-wave form
       hipLaunchKernelGGL(f ? decode_block16_fused_kernel : decode_block16_kernel, grid, dim3(256), 0, s, p);
     else if (cols <= 32)  // one 32-column block
-      hipLaunchKernelGGL(f ? decode_block_fused_kernel : decode_block_kernel, grid, dim3(512), 0, s, p);
+      hipLaunchKernelGGL(f ? decode_block_fused_kernel : decode_block_kernel, grid, dim3(256), 0, s, p);
     else if (p.n_cb == 1)  // one 48-column block
-      hipLaunchKernelGGL(f ? decode_block48_fused_kernel : decode_block48_kernel, grid, dim3(512), 0, s, p);
+      hipLaunchKernelGGL(f ? decode_block48_fused_kernel : decode_block48_kernel, grid, dim3(256), 0, s, p);
     else  // several 48-column blocks stream the same keys
-      hipLaunchKernelGGL(f ? decode_block48_shared_fused_kernel : decode_block48_shared_kernel, grid, dim3(512), 0,
+      hipLaunchKernelGGL(f ? decode_block48_shared_fused_kernel : decode_block48_shared_kernel, grid, dim3(256), 0,
                          s, p);
   }
   return hipGetLastError();
