@@ -27,12 +27,14 @@
 
 namespace duo {
 
-// LDS row pitches (bf16 elements). K rows are read 16 rows x one 16-byte
-// column per instruction (pitch = 4 dwords mod 64 banks keeps them apart);
-// V rows are read 4 rows x 32 bytes per 16-lane group by the transpose read
-// (pitch = 8 dwords mod 64 keeps those apart).
-constexpr int kPitch = kD + 8;    // K: 272 bytes
-constexpr int kVPitch = kD + 16;  // V: 288 bytes
+// LDS tiles are unpadded (256-byte rows) with their 16-byte chunks
+// XOR-swizzled by row: logical chunk c of row r sits at chunk c ^ (r & 15) of
+// a K row and c ^ 2 (r & 7) of a V row. A K fragment read (16 rows x one
+// chunk per 16 lanes) and a V transpose read (8 rows x 32 bytes per 32
+// lanes) then touch distinct banks, and one load instruction fills 4 whole
+// rows with its lanes in aligned 64-byte groups.
+constexpr int kPitch = kD;   // K and V rows: 256 bytes
+constexpr int kVPitch = kD;
 constexpr int kNegBig = -0x7fffffff;
 // Query rows per wave, in 16-row MFMA column blocks: 32 rows per wave. (64
 // rows per wave would halve the LDS operand reads per MFMA, but its
@@ -134,41 +136,30 @@ __device__ __forceinline__ TileAddr tile_addr(const KvSrc& s, int lo) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Direct global -> LDS loads of a K (kV = false) or V tile. The padded LDS
-// tile is a sequence of 16-byte slots, kSlots per row (16 data columns +
-// pad); one load instruction fills 64 consecutive slots, lane l slot 64 j + l,
-// and the tile's instructions are dealt round-robin to the waves. A pad
-// slot is filled with column 0 of its row (never read). The map holds, for
-// each of this wave's instructions, the tile row and the byte offset of the
-// column this lane fetches; it is the same for every tile.
-template <bool kV>
-struct SlotMap {
-  static constexpr int kSlots = (kV ? kVPitch : kPitch) / 8;
-  static constexpr int kInstr = kPrefillKeys * kSlots / 64;
-  static constexpr int kPerWave = (kInstr + kWaves - 1) / kWaves;
-  static_assert(kPrefillKeys * kSlots % 64 == 0, "tile must be whole load instructions");
-  uint32_t row[kPerWave];
-  uint32_t colb[kPerWave];
-
+// Direct global -> LDS loads of a K (kV = false) or V tile: 16 instructions
+// of 64 lanes x 16 bytes, instruction J filling rows 4 J .. 4 J + 3, dealt
+// round-robin to the waves (wave w takes J = w + 4 jj). Lane l of instruction
+// J fetches row 4 J + l / 16 at the logical chunk that the row's swizzle
+// puts in physical chunk l % 16; row & 15 (and row & 7) is the same for all
+// of a wave's instructions, so each lane's chunk is fixed.
+struct DmaLane {
+  uint32_t row;      // lane / 16: row within the instruction's 4
+  uint32_t kchunkb;  // byte offset of the K chunk this lane fetches
+  uint32_t vchunkb;  // byte offset of the V chunk this lane fetches
   __device__ __forceinline__ void init(int wave, int lane) {
-#pragma unroll
-    for (int jj = 0; jj < kPerWave; ++jj) {
-      const int slot = 64 * (wave + kWaves * jj) + lane;
-      const int rw = slot / kSlots;
-      const int col = slot - rw * kSlots;
-      row[jj] = (uint32_t)min(rw, kPrefillKeys - 1);
-      colb[jj] = col < 16 ? (uint32_t)col * 16u : 0u;
-    }
-  }
-  __device__ __forceinline__ static bool active(int wave, int jj) {
-    return kWaves * (jj + 1) <= kInstr || wave + kWaves * jj < kInstr;
+    row = (uint32_t)(lane >> 4);
+    const uint32_t r = 4u * (uint32_t)wave + row;  // tile row mod 16 of every instruction of this wave
+    kchunkb = (((uint32_t)lane & 15u) ^ (r & 15u)) * 16u;
+    vchunkb = (((uint32_t)lane & 15u) ^ (2u * (r & 7u))) * 16u;
   }
 };
+constexpr int kDmaPerWave = kPrefillKeys / 4 / kWaves;  // 4 instructions per wave and tile array
+static_assert(kPrefillKeys % (4 * kWaves) == 0, "tile must be whole load instructions per wave");
 
 template <bool kV>
 __device__ __forceinline__ void dma_tile(uint16_t* lds, const KvSrc& s, const TileRange& r, int lo,
-                                         const TileAddr& ta, int wave, const SlotMap<kV>& map) {
-  uint16_t* dst = lds + wave * 512;
+                                         const TileAddr& ta, int wave, const DmaLane& dl) {
+  const uint32_t chunkb = kV ? dl.vchunkb : dl.kchunkb;
   if (!ta.general) {
     // buffer loads from a raw buffer over the tile's rows (descriptor word
     // 3: 32-bit data format) + a 32-bit lane offset (row < 64, stride < 2^24
@@ -178,24 +169,23 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const KvSrc& s, const Ti
     // fragment reads keep their partial waits.
     const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(kV ? ta.v : ta.k), 0, (int)ta.bytes, 0x00020000);
+    const uint32_t lane_off = __umul24(dl.row, ta.stride_b) + chunkb;
 #pragma unroll
-    for (int jj = 0; jj < SlotMap<kV>::kPerWave; ++jj) {
-      if (SlotMap<kV>::active(wave, jj)) {
-        const uint32_t off = __umul24(map.row[jj], ta.stride_b) + map.colb[jj];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + jj * 512 * kWaves), 16, off, 0, 0, 0);
-      }
+    for (int jj = 0; jj < kDmaPerWave; ++jj) {
+      const int J = wave + kWaves * jj;
+      const uint32_t off = lane_off + (uint32_t)(4 * J) * ta.stride_b;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + J * 512), 16, off, 0, 0, 0);
     }
     return;
   }
 #pragma unroll
-  for (int jj = 0; jj < SlotMap<kV>::kPerWave; ++jj) {
-    if (SlotMap<kV>::active(wave, jj)) {
-      int pos = lo + (int)map.row[jj];
-      pos = pos < r.lo ? r.lo : (pos > r.hi ? r.hi : pos);
-      const Src rs = row_src(s, pos);
-      const char* src = reinterpret_cast<const char*>(kV ? rs.v : rs.k) + map.colb[jj];
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(dst + jj * 512 * kWaves), 16, 0, 0);
-    }
+  for (int jj = 0; jj < kDmaPerWave; ++jj) {
+    const int J = wave + kWaves * jj;
+    int pos = lo + 4 * J + (int)dl.row;
+    pos = pos < r.lo ? r.lo : (pos > r.hi ? r.hi : pos);
+    const Src rs = row_src(s, pos);
+    const char* src = reinterpret_cast<const char*>(kV ? rs.v : rs.k) + chunkb;
+    __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)(lds + J * 512), 16, 0, 0);
   }
   // the row-by-row form (tiles across start_pos or in a cache ring) waits
   // for its global loads here, so that none is in flight at the LDS reads
@@ -315,16 +305,14 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
   auto tile_lo = [&](int idx) {
     return idx < nt0 ? rg0.first + kPrefillKeys * idx : rg1.first + kPrefillKeys * (idx - nt0);
   };
-  SlotMap<false> kmap;
-  SlotMap<true> vmap;
-  kmap.init(wave, lane);
-  vmap.init(wave, lane);
+  DmaLane dl;
+  dl.init(wave, lane);
   auto issue = [&](int idx, uint16_t* dk, uint16_t* dv) {
     const TileRange& r = idx < nt0 ? rg0 : rg1;
     const int lo = tile_lo(idx);
     const TileAddr ta = tile_addr(src, lo);
-    dma_tile<false>(dk, src, r, lo, ta, wave, kmap);
-    dma_tile<true>(dv, src, r, lo, ta, wave, vmap);
+    dma_tile<false>(dk, src, r, lo, ta, wave, dl);
+    dma_tile<true>(dv, src, r, lo, ta, wave, dl);
   };
 
   // One tile: S^T = K Q^T, then start the next tile's loads into the other
@@ -339,7 +327,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
     bf16x8 kfirst[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
-      kfirst[kt] = *reinterpret_cast<const bf16x8*>(&cK[(16 * kt + r16) * kPitch + 8 * g]);
+      kfirst[kt] = *reinterpret_cast<const bf16x8*>(&cK[(16 * kt + r16) * kPitch + 8 * (g ^ r16)]);
     const bool first_range = idx < nt0;
     const TileRange r = first_range ? rg0 : rg1;
     const int lo = tile_lo(idx);
@@ -367,7 +355,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
         if (ds < 3) {
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
-            kb[(ds + 1) & 1][kt] = *reinterpret_cast<const bf16x8*>(&cK[(16 * kt + r16) * kPitch + 32 * (ds + 1) + 8 * g]);
+            kb[(ds + 1) & 1][kt] =
+                *reinterpret_cast<const bf16x8*>(&cK[(16 * kt + r16) * kPitch + 8 * ((4 * (ds + 1) + g) ^ r16)]);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -400,12 +389,17 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
       }
       // the first V fragments are read before the softmax, whose
       // arithmetic covers their latency; the rest stay 4 steps ahead
-      const uint16_t* vbase = &cV[(4 * g + (r16 >> 2)) * kVPitch + 4 * (r16 & 3)];
+      const int s7 = (4 * g + (r16 >> 2)) & 7;  // the V rows' swizzle, the same for every row this lane reads
+      const int vrow = (4 * g + (r16 >> 2)) * kVPitch + 4 * (r16 & 3);
+      // Each read address is one element offset from the tile array: the
+      // compiler tags an LDS access with its array only when the address is
+      // a short chain of offsets from it, and an untagged read waits for
+      // every load into LDS in flight (the next tile's included).
       i16x4 vr[4][2];
       auto vread = [&](int n, i16x4* d) {
-        const uint16_t* v0 = vbase + 32 * (n >> 3) * kVPitch + 16 * (n & 7);
-        d[0] = lds_read_tr16(v0);
-        d[1] = lds_read_tr16(v0 + 16 * kVPitch);
+        const int o = vrow + 32 * (n >> 3) * kVPitch + 16 * ((n & 7) ^ s7);
+        d[0] = lds_read_tr16(cV + o);
+        d[1] = lds_read_tr16(cV + (o + 16 * kVPitch));
       };
 #pragma unroll
       for (int n = 0; n < 4; ++n) vread(n, vr[n]);
