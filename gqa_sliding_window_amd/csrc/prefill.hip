@@ -209,6 +209,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
   __shared__ __attribute__((aligned(16))) uint16_t sV1[kPrefillKeys * kVPitch];
 
   __shared__ int s_last;
+  __shared__ int s_fin[8];  // work item fields for the finish (b, qhead, qa, qb, pieces used, unit, piece)
   const PrefillItem it = prefill_item(p, blockIdx.x);
   if (!it.valid) return;
 
@@ -264,6 +265,15 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
   const PieceRange pr = piece_range(ntiles, it.cls == kMain ? p.n_pieces : 1, it.piece);
   if (pr.t0 >= pr.t1) return;
   const int t_end = pr.t1;
+  if (tid == 0) {
+    s_fin[0] = it.b;
+    s_fin[1] = it.qhead;
+    s_fin[2] = qa;
+    s_fin[3] = qb;
+    s_fin[4] = pr.used;
+    s_fin[5] = it.unit;
+    s_fin[6] = it.piece;
+  }
 
   KvSrc src;
   src.cstride = (int64_t)p.hkv * kD;
@@ -484,26 +494,25 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
   for (int t = 0; t < kRT; ++t) l[t] = lane4_sum(l[t]);
 
   // The rest reads its parameters afresh from the kernel arguments (at an
-  // index the compiler cannot see is 0): keeping them in scalar registers
-  // across the tile loop spilled scalars there and cost the loop its
-  // overlapped LDS reads.
+  // index the compiler cannot see is 0) and the work item's fields from LDS,
+  // where the first thread left them: keeping them in scalar registers across
+  // the tile loop spilled scalars there and cost the loop its overlapped LDS
+  // reads, and recomputing the work item here cost a chain of dependent
+  // scalar steps at every workgroup's end.
   int zero = 0;
   __asm__ volatile("" : "+s"(zero));
   const PrefillParams& pf = (&p)[zero];
-  const PrefillItem itf = prefill_item(pf, blockIdx.x);
-  const int qheadf = itf.qhead + wave / kRowWaves;
+  const int fb = __builtin_amdgcn_readfirstlane(s_fin[0]);
+  const int fqhead = __builtin_amdgcn_readfirstlane(s_fin[1]);
+  const int qaf = __builtin_amdgcn_readfirstlane(s_fin[2]);
+  const int qbf = __builtin_amdgcn_readfirstlane(s_fin[3]);
+  const int fused = __builtin_amdgcn_readfirstlane(s_fin[4]);
+  const int funit = __builtin_amdgcn_readfirstlane(s_fin[5]);
+  const int fpiece = __builtin_amdgcn_readfirstlane(s_fin[6]);
+  const int qheadf = fqhead + wave / kRowWaves;
   const int Pf = (int)pf.start_pos;
-  const int qaf = Pf + itf.qtile * kRows;
-  const int qbf = min(qaf + kRows - 1, Pf + pf.T - 1);
   const int qw0f = qaf + rwave * 16 * kRT;
   const bool wave_activef = qw0f <= qbf;
-  PieceRange prf;
-  {
-    KeyRange k0, k1;
-    const int nr = prefill_key_ranges(pf, itf.cls, qaf, qbf, k0, k1);
-    const int nt = (int)tiles_of(k0) + (nr > 1 ? (int)tiles_of(k1) : 0);
-    prf = piece_range(nt, itf.cls == kMain ? pf.n_pieces : 1, itf.piece);
-  }
 
   // ---- key-range pieces: every piece publishes its partial (running max,
   // sum and unnormalised output, in the accumulator layout) with
@@ -512,11 +521,11 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
   // own included, and combines them in piece order (max, rescale, add), so
   // the result does not depend on which piece finished last; it finishes the
   // rows below and resets the counter for the next call.
-  if (prf.used > 1) {
+  if (fused > 1) {
     const int gw = pf.group / kHeads;  // workgroups per unit and piece
-    const int64_t cslot = (int64_t)itf.unit * gw + (itf.qhead - itf.kvh * pf.group) / kHeads;
+    const int64_t cslot = (int64_t)funit * gw + (fqhead % pf.group) / kHeads;
     const float* parts = pf.ws_part + cslot * pf.n_pieces * kPartFloats;
-    float* mine = pf.ws_part + (cslot * pf.n_pieces + itf.piece) * kPartFloats;
+    float* mine = pf.ws_part + (cslot * pf.n_pieces + fpiece) * kPartFloats;
 #pragma unroll
     for (int t = 0; t < kRT; ++t) {
 #pragma unroll
@@ -531,10 +540,10 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
     __syncthreads();
     int32_t* counter = pf.ws_count + cslot;
     if (tid == 0)
-      s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == prf.used - 1);
+      s_last = (__hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == fused - 1);
     __syncthreads();
     if (!s_last) return;
-    for (int q = 0; q < prf.used; ++q) {
+    for (int q = 0; q < fused; ++q) {
       const float* src = parts + (int64_t)q * kPartFloats;
 #pragma unroll
       for (int t = 0; t < kRT; ++t) {
@@ -573,7 +582,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
       inv = rn.inv;
       lse = rn.lse;
     }
-    const int64_t orow = ((int64_t)itf.b * pf.T + (qpos - Pf)) * pf.hq + qheadf;
+    const int64_t orow = ((int64_t)fb * pf.T + (qpos - Pf)) * pf.hq + qheadf;
     uint16_t* dst = pf.out + orow * kD + 4 * g;
     if (!kFused || pf.gate == nullptr) {
 #pragma unroll
@@ -599,7 +608,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
         *reinterpret_cast<bf16x4*>(dst + 16 * dt) = v;
       }
     }
-    if (pf.lse != nullptr && g == 0) pf.lse[((int64_t)itf.b * pf.hq + qheadf) * pf.T + (qpos - Pf)] = lse;
+    if (pf.lse != nullptr && g == 0) pf.lse[((int64_t)fb * pf.hq + qheadf) * pf.T + (qpos - Pf)] = lse;
   }
 }
 
