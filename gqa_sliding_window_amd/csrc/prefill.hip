@@ -568,7 +568,15 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
 
   if (!wave_activef) return;
   // ---- epilogue: O = O^T / l (with the attention sink, if any, in l), times
-  // the output gate, bf16 round-to-nearest-even; lse = (m + log2 l) ln 2
+  // the output gate, bf16 round-to-nearest-even; lse = (m + log2 l) ln 2.
+  // Each lane holds 4 consecutive columns of a row per 16-column block, so
+  // the rows go through LDS (the tile buffers are free after the loop's last
+  // barrier; one buffer per wave, 272-byte rows) and leave as whole 256-byte
+  // rows, 4 rows per store instruction, instead of 16 scattered 32-byte
+  // pieces per instruction.
+  constexpr int kOPitch = kD + 8;
+  static_assert(kPrefillWaveRows * kOPitch <= kPrefillKeys * kPitch, "staged rows must fit one tile buffer");
+  uint16_t* const stage = wave == 0 ? sK0 : (wave == 1 ? sV0 : (wave == 2 ? sK1 : sV1));
 #pragma unroll
   for (int t = 0; t < kRT; ++t) {
     const float lt = l[t];
@@ -583,7 +591,7 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
       lse = rn.lse;
     }
     const int64_t orow = ((int64_t)fb * pf.T + (qpos - Pf)) * pf.hq + qheadf;
-    uint16_t* dst = pf.out + orow * kD + 4 * g;
+    uint16_t* dst = stage + (16 * t + r16) * kOPitch + 4 * g;
     if (!kFused || pf.gate == nullptr) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt) {
@@ -609,6 +617,18 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
       }
     }
     if (pf.lse != nullptr && g == 0) pf.lse[((int64_t)fb * pf.hq + qheadf) * pf.T + (qpos - Pf)] = lse;
+  }
+  // the wave's own LDS writes are complete before its reads (one wave's LDS
+  // operations execute in order)
+#pragma unroll
+  for (int j = 0; j < kPrefillWaveRows / 4; ++j) {
+    const int row = 4 * j + g;
+    const int qpos = qw0f + row;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + row * kOPitch + 8 * r16);
+    if (qpos <= qbf) {
+      const int64_t orow = ((int64_t)fb * pf.T + (qpos - Pf)) * pf.hq + qheadf;
+      *reinterpret_cast<u32x4*>(pf.out + orow * kD + 8 * r16) = v;
+    }
   }
 }
 
