@@ -21,6 +21,10 @@ SLIDING = 1
 HEAD_DIM = 128
 
 DUO_OK = 0
+# duo_device_errors bits
+DEVICE_APPEND_PAST_CAPACITY = 1
+DEVICE_LENGTH_PAST_CAPACITY = 2
+DEVICE_LENGTH_PAST_PLAN = 4
 ERRORS = {-1: "DUO_ERR_INVALID_ARG", -2: "DUO_ERR_UNSUPPORTED", -3: "DUO_ERR_CAPACITY",
           -4: "DUO_ERR_WORKSPACE", -5: "DUO_ERR_HIP"}
 
@@ -129,6 +133,7 @@ def load(path: str = LIB_PATH):
         "duo_last_error": (ctypes.c_char_p, []),
         "duo_attn_version": (ctypes.c_int, []),
         "duo_prefill_tile_rows": (ctypes.c_int, [LP]),
+        "duo_device_errors": (ctypes.c_int, [ctypes.POINTER(ctypes.c_uint32), i32]),
     }
     for name, (res, args) in sigs.items():
         f = getattr(lib, name)
@@ -530,6 +535,15 @@ def attn_decode_block(layer: Layer, cache: KVCache, q, k_new, v_new, past_lens, 
 
 
 _plans = {}
+
+
+def device_errors(clear: bool = False) -> int:
+    """duo_device_errors: bits of out-of-contract device data the kernels
+    clamped on the current device since the last clear (waits for the
+    device)."""
+    bits = ctypes.c_uint32(0)
+    _check(load().duo_device_errors(ctypes.byref(bits), 1 if clear else 0))
+    return int(bits.value)
 
 
 def head_plan(layer: Layer):

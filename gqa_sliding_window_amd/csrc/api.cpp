@@ -381,6 +381,23 @@ int duo_prefill_tile_rows(const duo_layer* layer) {
 
 const char* duo_last_error(void) { return g_err; }
 
+int duo_device_errors(uint32_t* bits, int32_t clear) {
+  static_assert(kDevAppendPastCapacity == DUO_DEVICE_APPEND_PAST_CAPACITY &&
+                    kDevLengthPastCapacity == DUO_DEVICE_LENGTH_PAST_CAPACITY &&
+                    kDevLengthPastPlan == DUO_DEVICE_LENGTH_PAST_PLAN,
+                "device error bits match the header");
+  if (bits == nullptr) return fail(DUO_ERR_INVALID_ARG, "bits is NULL");
+  uint32_t v = 0u;
+  int rc = hip_status(hipDeviceSynchronize(), "device wait");
+  if (rc) return rc;
+  rc = hip_status(decode_device_errors(&v, clear != 0), "decode error word");
+  if (rc) return rc;
+  rc = hip_status(append_device_errors(&v, clear != 0), "append error word");
+  if (rc) return rc;
+  *bits = v;
+  return ok();
+}
+
 int duo_head_plan(const duo_layer* layer, int32_t* head_class, int32_t* head_rank_out, int32_t* n_main,
                   int32_t* n_stream) {
   Layer L;

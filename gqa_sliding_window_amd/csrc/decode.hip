@@ -252,6 +252,10 @@ __device__ __forceinline__ void write_out_pair(const DecodeParams& p, int64_t bh
 // items fill 512 resident slots (one 8-wave workgroup of 4 key slots per CU
 // left this workload's 514 non-empty items a second, partly filled round:
 // T = 4 / 6 / 8 147 / 172 / 179 -> 145 / 156 / 165 us).
+// Out-of-contract lengths the decode kernels clamped (duo_device_errors),
+// one word per device.
+__device__ unsigned int g_decode_errors;
+
 template <bool kBlock, int kNH, bool kFused, bool kShared = false>
 __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   static_assert(kNH == 1 || (kBlock && (kNH == 2 || kNH == 3)), "two or three column blocks only for the block decode");
@@ -296,8 +300,15 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
   const int n_valid = (int)decode_valid_slots(p, it.cls, len > 0 ? len : 0);  // < 2^31
   const int n_keys = n_valid + (kBlock ? T : 0);
   const int n_planned = (it.cls == kStream) ? p.n_split_stream : p.n_split_main;
-  int n_used = (n_keys + p.split_keys - 1) / p.split_keys;
-  if (n_used > n_planned) n_used = n_planned;  // a length beyond the planned maximum is cut
+  const int n_needed = (n_keys + p.split_keys - 1) / p.split_keys;
+  const int n_used = n_needed < n_planned ? n_needed : n_planned;  // a length beyond the planned maximum is cut
+  if (tid == 0 && it.split == 0 && cb == 0) {
+    // out-of-contract lengths, recorded once per (sequence, KV head)
+    unsigned bad = 0u;
+    if (it.cls != kStream && !p.main_ring && len > p.main_cap) bad |= kDevLengthPastCapacity;
+    if (n_needed > n_planned) bad |= kDevLengthPastPlan;
+    if (bad) atomicOr(&g_decode_errors, bad);
+  }
   const int64_t k_begin = (int64_t)it.split * p.split_keys;
   int64_t k_end = k_begin + p.split_keys;
   if (k_end > n_keys) k_end = n_keys;
@@ -850,6 +861,17 @@ hipError_t noalloc_scratch(void** ptr) {
   }
   *ptr = addr[dev];
   return hipSuccess;
+}
+
+hipError_t decode_device_errors(uint32_t* bits, bool clear) {
+  unsigned v = 0u;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_decode_errors), sizeof v, 0, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && clear && v != 0u) {
+    const unsigned z = 0u;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_decode_errors), &z, sizeof z, 0, hipMemcpyHostToDevice);
+  }
+  *bits |= v;
+  return e;
 }
 
 hipError_t launch_fill_zero(int32_t* p, int64_t n, hipStream_t s) {

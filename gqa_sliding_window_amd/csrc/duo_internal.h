@@ -345,6 +345,15 @@ __host__ __device__ inline int64_t decode_keys(const DecodeParams& p, int cls, i
   return decode_valid_slots(p, cls, len) + (block ? p.T : 0);
 }
 
+// Out-of-contract device data recorded by the kernels (bits of
+// duo_device_errors). Each kernel file keeps its own word per device; these
+// read them (after a device-wide wait) and optionally clear them.
+constexpr unsigned kDevAppendPastCapacity = 1u;
+constexpr unsigned kDevLengthPastCapacity = 2u;
+constexpr unsigned kDevLengthPastPlan = 4u;
+hipError_t decode_device_errors(uint32_t* bits, bool clear);
+hipError_t append_device_errors(uint32_t* bits, bool clear);
+
 // Launchers (defined in the .hip files).
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s);
 hipError_t launch_qk_prologue(const PrologueParams& p, hipStream_t s);

@@ -29,7 +29,12 @@ struct AppendDst {
   int pos;
 };
 
-__device__ __forceinline__ bool append_dst(const AppendParams& p, int64_t row, AppendDst& d) {
+// Positions dropped for lying past a contiguous main cache (duo_device_errors),
+// one word per device.
+__device__ unsigned int g_append_errors;
+
+// `lead`: the one lane of the row that records a dropped position.
+__device__ __forceinline__ bool append_dst(const AppendParams& p, int64_t row, bool lead, AppendDst& d) {
   const int kvh = (int)(row % p.hkv);
   const int64_t bt = row / p.hkv;
   const int t = (int)(bt % p.T);
@@ -59,7 +64,10 @@ __device__ __forceinline__ bool append_dst(const AppendParams& p, int64_t row, A
       if (pos < end - p.main_cap) return false;  // overwritten later in this call
       slot = pos % p.main_cap;
     } else {
-      if (pos >= p.main_cap) return false;       // outside the caller's buffer
+      if (pos >= p.main_cap) {                   // outside the caller's buffer
+        if (lead) atomicOr(&g_append_errors, kDevAppendPastCapacity);
+        return false;
+      }
       slot = pos;
     }
     head_base = ((int64_t)b * p.n_main + rank) * p.main_cap;
@@ -76,7 +84,7 @@ __global__ __launch_bounds__(256) void kv_append_kernel(AppendParams p) {
   const int chunk = threadIdx.x & 15;
   if (row >= (int64_t)p.batch * p.T * p.hkv) return;
   AppendDst d;
-  if (!append_dst(p, row, d)) return;
+  if (!append_dst(p, row, chunk == 0, d)) return;
   const int64_t src = row * kD + chunk * 8;
   const uint4 kv = *reinterpret_cast<const uint4*>(p.k_new + src);
   const uint4 vv = *reinterpret_cast<const uint4*>(p.v_new + src);
@@ -94,7 +102,7 @@ __global__ __launch_bounds__(256) void kv_append_pro_kernel(AppendParams p) {
   const int c = threadIdx.x & 7;
   if (row >= (int64_t)p.batch * p.T * p.hkv) return;
   AppendDst d;
-  if (!append_dst(p, row, d)) return;
+  if (!append_dst(p, row, c == 0, d)) return;
   const int64_t src = row * kD + 8 * c;
   float lo[8], hi[8];
   unpack8(*reinterpret_cast<const bf16x8*>(p.k_new + src), lo);
@@ -140,6 +148,17 @@ __global__ __launch_bounds__(256) void qk_prologue_kernel(PrologueParams p) {
   if (p.pr.rope) rope_block(lo, hi, c, pos, p.pr);
   *reinterpret_cast<bf16x8*>(p.y + src) = pack8(lo);
   *reinterpret_cast<bf16x8*>(p.y + src + 64) = pack8(hi);
+}
+
+hipError_t append_device_errors(uint32_t* bits, bool clear) {
+  unsigned v = 0u;
+  hipError_t e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_append_errors), sizeof v, 0, hipMemcpyDeviceToHost);
+  if (e == hipSuccess && clear && v != 0u) {
+    const unsigned z = 0u;
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_append_errors), &z, sizeof z, 0, hipMemcpyHostToDevice);
+  }
+  *bits |= v;
+  return e;
 }
 
 hipError_t launch_kv_append(const AppendParams& p, hipStream_t s) {

@@ -415,6 +415,29 @@ int duo_prefill_tile_rows(const duo_layer* layer);
 int duo_decode_plan(const duo_layer* layer, int32_t batch, int64_t max_seq_len,
                     int32_t* split_keys, int32_t* items, int64_t* n_items);
 
+/* Out-of-contract device data that kernels had to clamp (host only; a
+ * checked mode for debugging). Device-side arguments (start_pos, seq_lens,
+ * past_lens) cannot be validated before launch; where they break the
+ * contracts above, the kernels keep every access inside the caller's buffers
+ * (as those entries state) and record here that they did. Not defined by the
+ * pages: it checks the library's own contracts (duo_kv_cache slots, the
+ * max_seq_len / max_past_len bounds). Bits, or'ed since the last clear on the
+ * current device:
+ *   DUO_DEVICE_APPEND_PAST_CAPACITY: duo_kv_append dropped a position at or
+ *     past a contiguous main cache's capacity;
+ *   DUO_DEVICE_LENGTH_PAST_CAPACITY: a decode took a length past a
+ *     contiguous main cache's capacity as that capacity;
+ *   DUO_DEVICE_LENGTH_PAST_PLAN: a decode cut a length beyond its
+ *     max_seq_len / max_past_len bound to the planned splits.
+ * bits  : host output.
+ * clear : nonzero zeroes the bits after they are read.
+ * Waits for all work on the current device first. Calls still being issued
+ * by other threads may set bits after the read. */
+#define DUO_DEVICE_APPEND_PAST_CAPACITY 1u
+#define DUO_DEVICE_LENGTH_PAST_CAPACITY 2u
+#define DUO_DEVICE_LENGTH_PAST_PLAN 4u
+int duo_device_errors(uint32_t* bits, int32_t clear);
+
 const char* duo_last_error(void);
 int duo_attn_version(void);
 

@@ -111,6 +111,11 @@ int main(void) {
     CHECK(strlen(duo_last_error()) > 0);
   }
 
+  /* the device error word: a NULL output is refused before any device call */
+  CHECK(duo_device_errors(NULL, 0) == DUO_ERR_INVALID_ARG);
+  CHECK(DUO_DEVICE_APPEND_PAST_CAPACITY == 1u && DUO_DEVICE_LENGTH_PAST_CAPACITY == 2u &&
+        DUO_DEVICE_LENGTH_PAST_PLAN == 4u);
+
   /* empty calls are no-ops */
   CHECK(duo_attn_prefill(&L, NULL, 0, NULL, NULL, NULL, 0, 0, NULL, NULL, NULL, 0, NULL, NULL, NULL) == DUO_OK);
   printf("ok\n");
