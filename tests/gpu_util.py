@@ -22,12 +22,17 @@ def bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
 
 
-def check_close(got: np.ndarray, ref: np.ndarray, what: str, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
+def check_close(got: np.ndarray, ref: np.ndarray, what: str, max_abs=MAX_ABS, mean_abs=MEAN_ABS, rel=0.0):
+    """Elementwise |got - ref| <= max_abs + rel |ref|, and the mean error
+    <= mean_abs."""
     err = np.abs(got - ref)
     mx, mn = float(err.max()), float(err.mean())
     print(f"[parity] {what}: n={err.shape[0]} max_abs={mx:.3e} mean_abs={mn:.3e}", file=sys.stderr, flush=True)
     assert np.isfinite(got).all(), f"{what}: non-finite output"
-    assert mx <= max_abs, f"{what}: max abs error {mx:.3e} > {max_abs}"
+    over = err - (max_abs + rel * np.abs(ref))
+    worst = np.unravel_index(int(np.argmax(over)), over.shape)
+    assert over[worst] <= 0, (f"{what}: error {err[worst]:.3e} at {worst} (reference {ref[worst]:.4f}) "
+                              f"> {max_abs} + {rel} |reference|")
     assert mn <= mean_abs, f"{what}: mean abs error {mn:.3e} > {mean_abs}"
     return mx, mn
 

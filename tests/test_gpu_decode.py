@@ -54,7 +54,7 @@ def run_decode(lib, layer, cache, q, lengths, max_len, ws=None):
     return host_bits(out), lse.cpu().numpy()
 
 
-def check_decode(layer, q, seqs, out, lse, what):
+def check_decode(layer, q, seqs, out, lse, what, **tol):
     B, hq, _ = q.shape
     rows = [(b, h) for b in range(B) for h in range(hq) if seqs.L[b] > 0]
     o_ref, l_ref = oracle.decode_rows(q, seqs.kv_of, np.asarray(seqs.L), rows,
@@ -62,7 +62,7 @@ def check_decode(layer, q, seqs, out, lse, what):
                                       window=layer.window, sink=layer.sink, recent=layer.recent,
                                       full_attention_heads=layer.full_attention_heads)
     r = np.asarray(rows)
-    check_close(bits_to_f64(out[r[:, 0], r[:, 1]]), o_ref, what)
+    check_close(bits_to_f64(out[r[:, 0], r[:, 1]]), o_ref, what, **tol)
     err = np.abs(lse[r[:, 0], r[:, 1]] - l_ref).max()
     assert err < 1e-3, f"{what}: lse error {err}"
 

@@ -24,15 +24,21 @@ def _kw(layer):
                 full_attention_heads=layer.full_attention_heads, scale=layer.scale)
 
 
-def run_block(lib, layer, past, T, seed, cap=None):
+def run_block(lib, layer, past, T, seed, cap=None, transform=None):
     """Fill the caches to past_b, run the block decode; returns (q, K/V per
-    sequence, out bits [B, T, Hq, D], lse [B, T, Hq])."""
+    sequence, out bits [B, T, Hq, D], lse [B, T, Hq]). transform(which, bits,
+    positions) -> bits, if given, reshapes the value distribution of q, k or
+    v (positions: the absolute position of each row of bits)."""
     import torch
     B, hq, hkv = len(past), layer.num_q_heads, layer.num_kv_heads
     ends = [p + T for p in past]
     k = wl.normal_tokens_ragged(seed, wl.K, [0] * B, ends, hkv, 128)
     v = wl.normal_tokens_ragged(seed, wl.V, [0] * B, ends, hkv, 128)
     q = wl.normal_tokens(seed, wl.Q, B, 0, T, hq, 128)
+    if transform is not None:
+        k = [transform("k", k[b], np.arange(ends[b])) for b in range(B)]
+        v = [transform("v", v[b], np.arange(ends[b])) for b in range(B)]
+        q = np.stack([transform("q", q[b], past[b] + np.arange(T)) for b in range(B)])
     cap = cap or max(max(past), 1)
     cache = lib.KVCache(layer, B, cap)
     for b in range(B):
@@ -51,7 +57,7 @@ def run_block(lib, layer, past, T, seed, cap=None):
     return q, k, v, host_bits(out), lse.cpu().numpy(), (cache, ws, kn, vn, pl, out, lse)
 
 
-def check_block(layer, past, T, q, k, v, out, lse, what):
+def check_block(layer, past, T, q, k, v, out, lse, what, **tol):
     B, hq = len(past), layer.num_q_heads
     got, ref, lg, lr = [], [], [], []
     for b in range(B):
@@ -62,7 +68,7 @@ def check_block(layer, past, T, q, k, v, out, lse, what):
         lg.append(lse[b, r[:, 2], r[:, 1]].astype(np.float64))
         ref.append(o_ref)
         lr.append(l_ref)
-    check_close(np.concatenate(got), np.concatenate(ref), what)
+    check_close(np.concatenate(got), np.concatenate(ref), what, **tol)
     err = np.abs(np.concatenate(lg) - np.concatenate(lr)).max()
     assert err < 1e-3, f"{what}: lse error {err}"
 

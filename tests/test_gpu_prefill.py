@@ -67,11 +67,11 @@ def run_chunked(lib, layer, q, k, v, chunk, want_lse=True, pieces=False):
     return host_bits(out), (lse.cpu().numpy() if want_lse else None)
 
 
-def compare_rows(layer, q, k, v, out_bits, lse, rows, what):
+def compare_rows(layer, q, k, v, out_bits, lse, rows, what, **tol):
     o_ref, l_ref = oracle.prefill_rows(q, k, v, 0, rows, **_layer_kw(layer))
     r = np.asarray(rows)
     got = bits_to_f64(out_bits[r[:, 0], r[:, 2], r[:, 1]])
-    check_close(got, o_ref, what)
+    check_close(got, o_ref, what, **tol)
     if lse is not None:
         lg = lse[r[:, 0], r[:, 1], r[:, 2]].astype(np.float64)
         err = np.abs(lg - l_ref).max()
