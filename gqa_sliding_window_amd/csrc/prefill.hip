@@ -300,12 +300,16 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
 
   // ---- running state (log2 domain: x = s * scale * log2 e)
   const float c = p.scale_log2;
-  float m[kRT], l[kRT];
+  // thr = m + the rescale threshold and nmu = -m (0 while m is -inf) change
+  // only when the maximum moves, so the tile loop reads them ready-made
+  float m[kRT], l[kRT], thr[kRT], nmu[kRT];
   f32x4 o[kRT][8];
 #pragma unroll
   for (int t = 0; t < kRT; ++t) {
     m[t] = kNegInf;
     l[t] = 0.f;
+    thr[t] = kNegInf;
+    nmu[t] = 0.f;
   }
 #pragma unroll
   for (int t = 0; t < kRT; ++t)
@@ -419,7 +423,6 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
       // some lane's logits exceed it by the rescale threshold, so the
       // cross-lane exchange is skipped on most tiles.
       float lmx[kRT];
-      bool grow = false;
 #pragma unroll
       for (int t = 0; t < kRT; ++t) {
         // chained three-way maxima: 8 instructions for 16 values
@@ -429,15 +432,21 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
           v = fmaxf(fmaxf(v, s[t][j >> 2][j & 3]), s[t][(j + 1) >> 2][(j + 1) & 3]);
         v = fmaxf(v, s[t][3][3]);
         lmx[t] = v * c;
-        grow = grow || lmx[t] > m[t] + kRescaleThreshold;
       }
-      if (__any(grow)) {
+      static_assert(kRT == 2, "the rescale test below names both row blocks");
+      // one lane mask per row block, or-ed as scalars: a single ballot of the
+      // two tests or-ed per lane made the compiler copy the lane mask into a
+      // vector register and compare it back (two more vector instructions)
+      const uint64_t grow = __builtin_amdgcn_ballot_w64(lmx[0] > thr[0]) | __builtin_amdgcn_ballot_w64(lmx[1] > thr[1]);
+      if (grow != 0) {
 #pragma unroll
         for (int t = 0; t < kRT; ++t) {
           const float mx = lane4_max(lmx[t]);
           const bool up = mx > m[t] + kRescaleThreshold;
           const float a = up ? fast_exp2(m[t] - mx) : 1.f;
           m[t] = up ? mx : m[t];
+          thr[t] = m[t] + kRescaleThreshold;
+          nmu[t] = (m[t] == kNegInf) ? 0.f : -m[t];
           l[t] *= a;
 #pragma unroll
           for (int dt = 0; dt < 8; ++dt) o[t][dt] *= a;
@@ -446,15 +455,14 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
       bf16x8 pb[kRT][2];
 #pragma unroll
       for (int t = 0; t < kRT; ++t) {
-        const float mu = (m[t] == kNegInf) ? 0.f : m[t];
-        float sum = 0.f;
+        float sum;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float e = fast_exp2(__builtin_fmaf(s[t][kt][i], c, -mu));
+            const float e = fast_exp2(__builtin_fmaf(s[t][kt][i], c, nmu[t]));
             s[t][kt][i] = e;
-            sum += e;
+            sum = (kt == 0 && i == 0) ? e : sum + e;
           }
         l[t] += sum;
         pb[t][0] = pack_bf16(s[t][0], s[t][1]);
