@@ -307,17 +307,35 @@ def bench_chunked(torch, G, wl, timer, warmup, steps):
             G.attn_prefill(layer, q[c], k[c], v[c], out[c], start_pos=c * w.chunk, past=cache, workspace=ws)
             G.kv_append(layer, cache, k[c], v[c], starts[c], max_end_pos=(c + 1) * w.chunk)
 
-    log("chunked prefill: timing passes")
-    ms = timer.run(one_pass, warmup, steps)
-    pass_stats = dict(timer.last)
     # attention alone: the 16 prefill calls of a pass without their appends
-    # (the cache already holds every position), timed like the passes
+    # (the cache already holds every position)
     def attend_only(_):
         for c in range(n_chunks):
             G.attn_prefill(layer, q[c], k[c], v[c], out[c], start_pos=c * w.chunk, past=cache, workspace=ws)
 
-    log("chunked prefill: timing the attention calls alone")
-    attn_ms = timer.run(attend_only, warmup, steps)
+    # The two kinds of pass alternate, each between its own event pair, so
+    # that clock drift over the run does not favour whichever is timed first
+    # (the appends are 16 short kernels, about 0.3% of a pass).
+    log("chunked prefill: timing passes (attend + append, attention alone, interleaved)")
+    for i in range(warmup):
+        one_pass(i)
+        attend_only(i)
+    torch.cuda.synchronize()
+    s = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
+    ev[0].record(s)
+    for i in range(steps):
+        one_pass(i)
+        ev[2 * i + 1].record(s)
+        attend_only(i)
+        ev[2 * i + 2].record(s)
+    torch.cuda.synchronize()
+    tot = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps))
+    att = sorted(ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(steps))
+    ms = sum(tot) / steps
+    attn_ms = sum(att) / steps
+    pass_stats = {"median_ms": tot[steps // 2], "min_ms": tot[0], "passes": steps,
+                  "attention_only_median_ms": att[steps // 2], "attention_only_min_ms": att[0]}
     # cache manager on one chunk: read 2 x chunk rows, write 2 x chunk rows
     app_ms = timer.run(lambda i: G.kv_append(layer, cache, k[0], v[0], starts[0], max_end_pos=w.chunk), 2, 20)
     app_bytes = 2 * 2 * w.chunk * w.hkv * 128 * 2
@@ -543,12 +561,14 @@ def main():
 
     if "chunked" in sections:
         w5, mask5, fl5, ms5, attn5, app_ms, app_bytes, st5, pieces5, ws5 = bench_chunked(
-            torch, G, wl, timer, 1, max(1, args.steps // 10))
+            torch, G, wl, timer, 1, max(3, args.steps // 4))
         res["chunked_prefill"] = {"workload": w5.name, "mask": mask5, "algorithmic_flop": fl5,
                                   "ms_total": ms5, "TFLOP/s": fl5 / (ms5 * 1e-3) / 1e12,
                                   "ms_total_median": st5["median_ms"], "ms_total_min": st5["min_ms"],
                                   "pieces_per_chunk": pieces5, "prefill_workspace_bytes": ws5,
                                   "attention_only_ms": attn5,
+                                  "attention_only_ms_median": st5["attention_only_median_ms"],
+                                  "passes_each": st5["passes"],
                                   "attention_only_TFLOP/s": fl5 / (attn5 * 1e-3) / 1e12}
         res["kv_append"] = {"workload": "one 8192-token chunk, 8 KV heads", "ms": app_ms,
                             "GB/s": app_bytes / (app_ms * 1e-3) / 1e9}
