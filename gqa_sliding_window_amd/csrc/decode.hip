@@ -176,9 +176,9 @@ __device__ __forceinline__ void attend_tile(const uint16_t* sK, const uint16_t* 
   for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kt][i]);
-  mx = wave_xor_max(mx, 16);
-  mx = wave_xor_max(mx, 32);
-  mx *= c;
+  // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same column: row swaps on the
+  // VALU (a shuffle is an LDS round trip, twice per tile on the attend path)
+  mx = lane4_max(mx) * c;
   const bool up = mx > m + kRescaleThreshold;
   if (__any(up)) {
     const float a = up ? fast_exp2(m - mx) : 1.f;
@@ -618,8 +618,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
         for (int dt = 0; dt < 8; ++dt) sec.o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
       stream(std::integral_constant<int, 6>{}, std::integral_constant<int, 0>{}, std::true_type{}, sec);
-      sec.l += __shfl_xor(sec.l, 16);
-      sec.l += __shfl_xor(sec.l, 32);
+      sec.l = lane4_sum(sec.l);
       // every wave is past its last tile: block 2's partial into the
       // combine area (over the tiles)
       __syncthreads();
@@ -637,8 +636,7 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
       __syncthreads();
     }
   }
-  l += __shfl_xor(l, 16);
-  l += __shfl_xor(l, 32);
+  l = lane4_sum(l);
 
   // ---- combine the key slots: acc[slot][col][dim] in LDS (reuses the tile area)
   __syncthreads();

@@ -58,10 +58,6 @@ __device__ __forceinline__ bf16x4 pack_bf16x4(const f32x4& v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float wave_xor_max(float v, int mask) {
-  return fmaxf(v, __shfl_xor(v, mask));
-}
-
 // Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 on the VALU (no LDS
 // instruction): each row swap leaves lane l's value and its partner's, in the
 // other 16-lane (then 32-lane) half, in the two results.
