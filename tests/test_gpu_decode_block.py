@@ -144,10 +144,11 @@ def test_block_workspace_reuse_and_smaller_call(lib):
     check_block(layer, past, T2, q[:, :T2], k, v, host_bits(o3), l3.cpu().numpy(), "reuse call 3 (T=3)")
 
 
-@pytest.mark.parametrize("T", [4, 8])
+@pytest.mark.parametrize("T", [4, 6, 8])
 def test_block_decode_duo_workload(lib, T):
     """The verify-block launches the bench times: T = 4 (24 columns, one
-    32-column block) and T = 8 (48 columns, one 48-column block) tokens
+    32-column block), T = 6 (36 columns, a partly filled 48-column block)
+    and T = 8 (48 columns, one 48-column block) tokens
     after the Duo decode workload's contexts (batch 16, 48/8
     heads, contexts U[32768, 131072], its Bernoulli(0.25) mask), every row
     against the oracle."""
