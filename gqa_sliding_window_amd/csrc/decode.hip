@@ -522,8 +522,9 @@ __device__ __forceinline__ void decode_body(const DecodeParams& p) {
     // 48 columns, the cache streamed once: a 32-key tile is 16 groups of 4
     // rows (8 of K, 8 of V); the waves of half 0, which attend two column
     // blocks, load 6 groups of each tile, those of half 1 the other 10, so
-    // that both fit their registers with four tiles in flight (the same
-    // bytes in flight per CU as the 32-column form).
+    // that both fit their registers with three tiles in flight (three
+    // quarters of the 32-column form's bytes in flight per CU; four tiles
+    // spilled 72 registers).
     uint16_t* sK0 = smem + slot * 4 * kTileElems;
     uint16_t* sV0 = sK0 + kTileElems;
     uint16_t* sK1 = sV0 + kTileElems;
