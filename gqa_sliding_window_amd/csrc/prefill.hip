@@ -50,6 +50,27 @@ struct TileRange {
   int first;       // first tile start (lo rounded down to 64)
 };
 
+// A wave's per-tile tests on a key range, as intervals of the tile start lo
+// (keys lo .. lo + 63), formed once per work item: the tile is visible to
+// the wave's rows [qw0, qw1] when vlo <= lo <= vhi, and every key of it is
+// visible to every one of those rows when mlo <= lo <= mhi.
+struct TileTest {
+  int vlo, vhi, mlo, mhi;
+};
+
+__device__ __forceinline__ TileTest tile_test(const TileRange& r, int qw0, int qw1, bool wave_active) {
+  constexpr int64_t kLow = kNegBig;
+  TileTest t;
+  // some key lo .. lo + 63 in the band of row qw0: lo + 63 >= qw0 - span + 1;
+  // some key not after row qw1: lo <= qw1
+  t.vlo = r.span > 0 ? (int)max((int64_t)qw0 - r.span - (kPrefillKeys - 2), kLow) : kNegBig;
+  t.vhi = wave_active ? qw1 : kNegBig;
+  // lo >= r.lo, lo + 63 <= min(r.hi, qw0), lo >= qw1 - span + 1
+  t.mlo = r.span > 0 ? (int)max((int64_t)r.lo, (int64_t)qw1 - r.span + 1) : r.lo;
+  t.mhi = min(r.hi, qw0) - (kPrefillKeys - 1);
+  return t;
+}
+
 struct Src {
   const uint16_t* k;
   const uint16_t* v;
@@ -259,6 +280,8 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
       ntiles += (int)tiles_of(k1);
     }
   }
+  const TileTest tt0 = tile_test(rg0, qw0, qw1, wave_active);
+  const TileTest tt1 = tile_test(rg1, qw0, qw1, wave_active);
   // this workgroup's piece of the unit's tiles (a main unit may be cut into
   // key-range pieces that are merged below; the later pieces of a short unit
   // are empty)
@@ -316,9 +339,10 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt) o[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto tile_lo = [&](int idx) {
-    return idx < nt0 ? rg0.first + kPrefillKeys * idx : rg1.first + kPrefillKeys * (idx - nt0);
-  };
+  // tile idx starts at base + 64 idx, with the second range's base moved
+  // back by its first tile's index (|values| stay below 2^31)
+  const int tb0 = rg0.first, tb1 = rg1.first - kPrefillKeys * nt0;
+  auto tile_lo = [&](int idx) { return (idx < nt0 ? tb0 : tb1) + kPrefillKeys * idx; };
   DmaLane dl;
   dl.init(wave, lane);
   auto issue = [&](int idx, uint16_t* dk, uint16_t* dv) {
@@ -343,10 +367,9 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
     for (int kt = 0; kt < 4; ++kt)
       kfirst[kt] = *reinterpret_cast<const bf16x8*>(&cK[(16 * kt + r16) * kPitch + 8 * (g ^ r16)]);
     const bool first_range = idx < nt0;
-    const TileRange r = first_range ? rg0 : rg1;
+    const TileTest tt = first_range ? tt0 : tt1;
     const int lo = tile_lo(idx);
-    const int hi = lo + kPrefillKeys - 1;
-    const bool invisible = !wave_active || lo > qw1 || (r.span > 0 && hi < qw0 - r.span + 1);
+    const bool invisible = lo < tt.vlo || lo > tt.vhi;
 
     // S^T = K Q^T for 64 keys x 16 kRT rows, and the next tile's load issue,
     // at raised wave priority: the SIMD's other wave is then in its softmax
@@ -383,8 +406,9 @@ __device__ __forceinline__ void prefill_body(const PrefillParams& p) {
     if (idx + 1 < t_end) issue(idx + 1, nK, nV);
     __builtin_amdgcn_s_setprio(0);
     if (!invisible) {
-      const bool need_mask = !(lo >= r.lo && hi <= r.hi && hi <= qw0 && (r.span == 0 || lo >= qw1 - r.span + 1));
+      const bool need_mask = lo < tt.mlo || lo > tt.mhi;
       if (need_mask) {
+        const TileRange r = first_range ? rg0 : rg1;
         // row q sees keys in [klo, khi]
 #pragma unroll
         for (int t = 0; t < kRT; ++t) {
